@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for linear attention with phi(x) = elu(x) + 1.
+
+Test infrastructure only: the tests, the smoke check and the CPU-baseline leg of
+the benchmark import it; the product path never does.  It shares no code with
+the HIP library (see ``la_oracle.c`` for the arithmetic and its sources).
+"""
+from .oracle import (  # noqa: F401
+    build,
+    fwd_causal,
+    fwd_noncausal,
+    decode_step,
+    bwd_causal,
+    num_threads,
+    library_path,
+    load_variant,
+    source_path,
+)
