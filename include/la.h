@@ -1,0 +1,156 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) linear-attention library, liblinattn.so.
+ *
+ * Linear attention with the feature map phi(x) = elu(x) + 1 (ELU slope 1):
+ * phi(x) = x + 1 for x > 0 and exp(x) otherwise.  Sources, by page and section
+ * ("Transformers are RNNs" blog digest by irregular6612, the velog review
+ * "[논문 리뷰] Transformers are RNNs", and the itwiki article "선형 어텐션"):
+ *   - feature map and kernelised similarity sim(q,k) = phi(q).phi(k): blog
+ *     digest "Methods"; velog 3.2-3.3; itwiki "Formulas";
+ *   - non-causal form phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1): blog digest
+ *     "Method / key components 2)"; velog 3.2; itwiki "reordering by
+ *     associativity";
+ *   - causal prefix sums S_i = sum_{j<=i} phi(k_j) v_j^T, z_i = sum_{j<=i}
+ *     phi(k_j), out_i = phi(q_i)^T S_i / phi(q_i)^T z_i: blog digest
+ *     "key components 3)"; velog 3.4; itwiki "Causal masking and the
+ *     recurrent form";
+ *   - chunked evaluation (matrix products inside a chunk, state carried
+ *     between chunks): itwiki table "Comparison of forms" and the remark that
+ *     training kernels use the chunked form;
+ *   - recurrent step S += phi(k) v^T, z += phi(k), then read: blog digest
+ *     "key components 4)"; velog 3.6; itwiki "Causal masking and the
+ *     recurrent form";
+ *   - gradient as cumulative sums with linear memory: velog 3.5; blog digest
+ *     "Methods" (last item).
+ *
+ * Conventions shared by every entry point
+ *   Layout    All tensors are dense, row-major and contiguous:
+ *             sequences [B][H][N][d], state S [B][H][d_k][d_v],
+ *             normaliser z [B][H][d_k], per-token denominators [B][H][N],
+ *             per-step decode vectors [B][H][d].  Every pointer must be
+ *             16-byte aligned.
+ *   Sizes     d_k, d_v in {16, 32, 64, 128}, chosen independently; N >= 1 and
+ *             need not be a multiple of C; C in {16, 32, 64}; B, H >= 1.
+ *   Dtypes    `in` is the storage type of q, k, v (and dO, dq, dk, dv);
+ *             `out` that of o.  S, z and den are always fp32.  Arithmetic is
+ *             fp32 accumulate; for LA_BF16 inputs the matrix products take
+ *             bf16 operands (MFMA), for LA_F32 inputs they stay in fp32.
+ *   Ownership The caller allocates every buffer, including the workspace
+ *             (size from the matching *_workspace_bytes query); the library
+ *             allocates nothing and keeps no state between calls.
+ *   Streams   Every call only enqueues work on `stream` (0 = the null stream)
+ *             and returns; results are ready when the stream has reached it.
+ *   Errors    All arguments are checked before anything is enqueued; a bad
+ *             argument returns a non-zero la_status and launches nothing.  A
+ *             failed launch returns LA_ERR_LAUNCH.  NaN or Inf inputs are
+ *             propagated, not reported.  No C++ exception crosses the ABI.
+ *             No denominator epsilon is added: inputs below about -87 make
+ *             exp underflow in fp32, and a zero denominator then yields Inf
+ *             or NaN, as the formulas imply.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL_PTR = 1,     /* a required pointer is NULL                       */
+    LA_ERR_BAD_SHAPE = 2,    /* B, H or N out of range                           */
+    LA_ERR_UNSUPPORTED = 3,  /* d_k, d_v or C outside the supported sets         */
+    LA_ERR_BAD_DTYPE = 4,    /* unknown la_dtype value                           */
+    LA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the query says    */
+    LA_ERR_LAUNCH = 6,       /* the HIP runtime rejected a launch                */
+    LA_ERR_ALIGNMENT = 7     /* a pointer is not 16-byte aligned                 */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *la_status_string(la_status s);
+
+/* Workspace bytes each entry point needs for these sizes (0 is a valid
+ * answer: then `ws` may be NULL).  Invalid sizes return 0; the entry point
+ * itself reports the error. */
+size_t la_fwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C);
+size_t la_fwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v);
+size_t la_bwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C);
+
+/*
+ * Non-causal forward: o_i = phi(q_i)^T (sum_j phi(k_j) v_j^T) /
+ *                           phi(q_i)^T (sum_j phi(k_j)),  sums over all N.
+ * q, k: [B][H][N][d_k] (in); v: [B][H][N][d_v] (in); o: [B][H][N][d_v] (out).
+ */
+la_status la_fwd_noncausal(const void *q, const void *k, const void *v, void *o,
+                           int B, int H, int N, int d_k, int d_v,
+                           la_dtype in, la_dtype out,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Causal forward, evaluated chunk by chunk (C tokens per chunk):
+ *   o_i = phi(q_i)^T S_i / den_i,  den_i = phi(q_i)^T z_i,
+ *   S_i = sum_{j<=i} phi(k_j) v_j^T,  z_i = sum_{j<=i} phi(k_j).
+ * The result does not depend on C (the chunked form is an exact rewrite);
+ * C only sets the tiling.  den (nullable, fp32 [B][H][N]) receives den_i,
+ * which la_bwd_causal needs.
+ */
+la_status la_fwd_causal(const void *q, const void *k, const void *v, void *o, float *den,
+                        int B, int H, int N, int d_k, int d_v, int C,
+                        la_dtype in, la_dtype out,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Causal forward with a carried state (prefill that hands over to decode):
+ * as la_fwd_causal, but the prefix sums start from S0, z0 instead of zero
+ * (S0 [B][H][d_k][d_v], z0 [B][H][d_k], fp32, both NULL for a zero start),
+ * and the state after the last token is written to S_out, z_out (fp32, both
+ * NULL to skip).  S_out/z_out may alias S0/z0.  With S_out, z_out from one
+ * call passed as S0, z0 to the next, two calls over the halves of a sequence
+ * give the same outputs as one call over the whole, and S_out, z_out seed
+ * la_decode_step.
+ */
+la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void *o, float *den,
+                              const float *S0, const float *z0, float *S_out, float *z_out,
+                              int B, int H, int N, int d_k, int d_v, int C,
+                              la_dtype in, la_dtype out,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Causal backward by cumulative sums (exact gradient of la_fwd_causal).
+ * With g_i = dO_i, gh_i = g_i / den_i and eps_i = -(g_i . o_i) / den_i:
+ *   dphi(q_i) = S_i gh_i + eps_i z_i                (forward prefix sums)
+ *   dphi(k_j) = R_j v_j + r_j,  dv_j = R_j^T phi(k_j)  (reverse suffix sums)
+ *   with R_j = sum_{i>=j} phi(q_i) gh_i^T, r_j = sum_{i>=j} phi(q_i) eps_i,
+ *   then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).
+ * Inputs: q, k, v, o (as produced by la_fwd_causal, storage type `in`), den
+ * (fp32, from la_fwd_causal), dO [B][H][N][d_v].  Outputs dq, dk
+ * [B][H][N][d_k] and dv [B][H][N][d_v] in `in`.  No per-token state is
+ * stored; workspace holds per-segment d_k x (d_v + 1) sums.
+ */
+la_status la_bwd_causal(const void *q, const void *k, const void *v, const void *o,
+                        const float *den, const void *dO,
+                        void *dq, void *dk, void *dv,
+                        int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step for every (b, h):
+ *   S += phi(k) v^T;  z += phi(k);  o = phi(q)^T S / (phi(q) . z)
+ * (update first, then read).  S [B][H][d_k][d_v] and z [B][H][d_k] are fp32,
+ * read and written in place; the caller zeroes them before the first step.
+ * q, k: [B][H][d_k], v: [B][H][d_v] and o: [B][H][d_v] in `in`.
+ */
+la_status la_decode_step(float *S, float *z, const void *q, const void *k, const void *v,
+                         void *o, int B, int H, int d_k, int d_v, la_dtype in,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

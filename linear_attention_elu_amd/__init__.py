@@ -1,0 +1,17 @@
+"""MI355X (gfx950) linear attention with phi(x) = elu(x) + 1.
+
+The computation lives in liblinattn.so (hand-written HIP kernels behind the C
+ABI in include/la.h); the functions here only marshal torch tensors to it.
+"""
+from ._lib import LAError, LIB_PATH, EXPORTS, load  # noqa: F401
+from .binding import (  # noqa: F401
+    la_status_string,
+    la_fwd_causal_workspace_bytes,
+    la_fwd_noncausal_workspace_bytes,
+    la_bwd_causal_workspace_bytes,
+    la_fwd_causal,
+    la_fwd_causal_state,
+    la_fwd_noncausal,
+    la_bwd_causal,
+    la_decode_step,
+)

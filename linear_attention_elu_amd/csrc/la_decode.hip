@@ -1,0 +1,129 @@
+// la_decode.hip -- one recurrent decode step for every (batch, head) on gfx950.
+//
+// Recurrent form (blog digest "Method / key components 4)"; velog review 3.6
+// "Transformers and RNNs"; itwiki "선형 어텐션", section "Causal masking and
+// the recurrent form"): S += phi(k) v^T, z += phi(k), then
+// o = phi(q)^T S / phi(q)^T z, the update coming before the read.
+//
+// The step is bound by streaming the fp32 state through HBM (read and write
+// d_k x d_v floats per (batch, head) against O(d) other bytes), so the kernel
+// is plain VALU work laid out for coalescing: one wave per (batch, head);
+// the wave's lanes cover a row of S with 16-byte accesses (d_v / 4 lanes per
+// row) and 64 / (d_v / 4) rows at a time, so each wave-wide access is one
+// contiguous block of S.  Column sums of phi(q) * S are reduced across the
+// rows a wave holds with lane shuffles; phi(q) . z across the wave.
+#include "la_device.hpp"
+#include "la_internal.h"
+
+namespace la {
+
+template <int DK, int DV, typename TI>
+__global__ void __launch_bounds__(256)
+la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__restrict__ q,
+                 const void *__restrict__ k, const void *__restrict__ v, void *__restrict__ o, long BH) {
+    constexpr int CV = DV / 4;   // lanes per row of S (one float4 each)
+    constexpr int RG = 64 / CV;  // rows of S a wave covers per access
+    constexpr int RPL = DK / RG; // accesses per lane
+    const int lane = threadIdx.x & 63;
+    const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bh >= BH) return;  // whole waves leave; no block-wide barrier follows
+
+    const int cg = lane % CV;
+    const int r0 = lane / CV;
+    float *Sb = S + bh * (long)DK * DV;
+    const long qk0 = bh * (long)DK;
+
+    float vv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) vv[t] = Store<TI>::load(v, bh * (long)DV + 4 * cg + t);
+
+    // Accesses are issued in groups of up to eight so that loads overlap
+    // without holding the whole slice of S in registers.
+    constexpr int GRP = RPL < 8 ? RPL : 8;
+    float num[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t0 = 0; t0 < RPL; t0 += GRP) {
+        f32x4 sreg[GRP];
+#pragma unroll
+        for (int t = 0; t < GRP; ++t)
+            sreg[t] = *reinterpret_cast<const f32x4 *>(Sb + (long)(r0 + RG * (t0 + t)) * DV + 4 * cg);
+#pragma unroll
+        for (int t = 0; t < GRP; ++t) {
+            const int e = r0 + RG * (t0 + t);
+            const float fk = phi(Store<TI>::load(k, qk0 + e));
+            const float fq = phi(Store<TI>::load(q, qk0 + e));
+            f32x4 s = sreg[t];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                s[c] = s[c] + fk * vv[c];
+                num[c] += fq * s[c];
+            }
+            *reinterpret_cast<f32x4 *>(Sb + (long)e * DV + 4 * cg) = s;
+        }
+    }
+    // column sums over the RG row groups of the wave
+#pragma unroll
+    for (int off = CV; off < 64; off *= 2)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[c] += __shfl_xor(num[c], off, 64);
+
+    float dpart = 0.f;
+#pragma unroll
+    for (int h = 0; h < (DK + 63) / 64; ++h) {
+        const int e = lane + 64 * h;
+        if (e < DK) {
+            const float zn = z[qk0 + e] + phi(Store<TI>::load(k, qk0 + e));
+            z[qk0 + e] = zn;
+            dpart += phi(Store<TI>::load(q, qk0 + e)) * zn;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) dpart += __shfl_xor(dpart, off, 64);
+
+    if (lane < CV) {
+        const long ob = bh * (long)DV + 4 * cg;
+        if (sizeof(TI) == 4) {
+            f32x4 w = {num[0] / dpart, num[1] / dpart, num[2] / dpart, num[3] / dpart};
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + ob) = w;
+        } else {
+            uint2 w;
+            w.x = (uint32_t)f32_to_bf16_bits(num[0] / dpart) | ((uint32_t)f32_to_bf16_bits(num[1] / dpart) << 16);
+            w.y = (uint32_t)f32_to_bf16_bits(num[2] / dpart) | ((uint32_t)f32_to_bf16_bits(num[3] / dpart) << 16);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(o) + ob) = w;
+        }
+    }
+}
+
+template <int DK, int DV>
+static hipError_t run_decode_t(const DecodeDesc &d) {
+    const long BH = (long)d.B * d.H;
+    const dim3 grid((unsigned)((BH + 3) / 4));
+    if (d.in_bf16)
+        la_decode_kernel<DK, DV, __bf16><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH);
+    else
+        la_decode_kernel<DK, DV, float><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH);
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t run_decode_dk(const DecodeDesc &d) {
+    switch (d.DV) {
+        case 16: return run_decode_t<DK, 16>(d);
+        case 32: return run_decode_t<DK, 32>(d);
+        case 64: return run_decode_t<DK, 64>(d);
+        case 128: return run_decode_t<DK, 128>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t run_decode(const DecodeDesc &d) {
+    switch (d.DK) {
+        case 16: return run_decode_dk<16>(d);
+        case 32: return run_decode_dk<32>(d);
+        case 64: return run_decode_dk<64>(d);
+        case 128: return run_decode_dk<128>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace la

@@ -1,0 +1,190 @@
+// la_device.hpp -- device-side building blocks for the gfx950 kernels.
+//
+// MFMA fragment conventions (wave64, 16x16 tiles).  Lane l belongs to lane
+// group g = l / 16 and has position p = l % 16 inside the group.
+//   * A operand (16 x 32, M x K): lane l supplies row m = p and eight K values.
+//   * B operand (32 x 16, K x N): lane l supplies column n = p and eight K values.
+//   * Accumulator (16 x 16): lane l holds rows m = 4g + r (r = 0..3) of column n = p.
+// The hardware pairs A's and B's K values lane group by lane group and slot by
+// slot, so any assignment of the 32 K indices to (g, slot) works as long as
+// both operands use the same one.  Two assignments are used:
+//   * "straight": slot t of group g is K index 8g + t;
+//   * "split":    slot t < 4 of group g is 4g + t, slot t >= 4 is 16 + 4g + (t - 4).
+// The split assignment is exactly the row set an accumulator lane holds over
+// two stacked 16 x 16 tiles, so an accumulator can be fed back as an operand
+// without leaving registers.
+//
+// bf16 path: one v_mfma_f32_16x16x32_bf16 per 32-wide K step.
+// fp32 path: eight v_mfma_f32_16x16x4_f32, slot t of every group forming the
+// four K values of the t-th instruction -- the same pairing, in fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Scalar helpers
+// ---------------------------------------------------------------------------
+
+// phi(x) = elu(x) + 1 (slope 1): x + 1 above zero, exp(x) at or below zero.
+__device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+
+// phi'(x): 1 above zero, exp(x) at or below zero.
+__device__ __forceinline__ float dphi(float x) { return x > 0.0f ? 1.0f : __expf(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 f32_to_bf16(float x) { return static_cast<__bf16>(x); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 b = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float round_bf16(float x) {
+    return static_cast<float>(static_cast<__bf16>(x));
+}
+
+// ---------------------------------------------------------------------------
+// Compute-type traits: the type matrix operands are staged in (LDS and
+// registers) and the 32-wide K step built on it.
+// ---------------------------------------------------------------------------
+template <typename TC> struct Frag;
+
+template <> struct Frag<__bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = static_cast<__bf16>(0.0f);
+    }
+    __device__ __forceinline__ void set(int t, float x) { v[t] = static_cast<__bf16>(x); }
+    __device__ __forceinline__ float get(int t) const { return static_cast<float>(v[t]); }
+};
+
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = 0.0f;
+    }
+    __device__ __forceinline__ void set(int t, float x) { v[t] = x; }
+    __device__ __forceinline__ float get(int t) const { return v[t]; }
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag<__bf16> &a, const Frag<__bf16> &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b, f32x4 c) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[t], b.v[t], c, 0, 0, 0);
+    return c;
+}
+
+// Round a value to what the operand type can hold (identity for fp32).
+template <typename TC> __device__ __forceinline__ float to_operand(float x);
+template <> __device__ __forceinline__ float to_operand<__bf16>(float x) { return round_bf16(x); }
+template <> __device__ __forceinline__ float to_operand<float>(float x) { return x; }
+
+// ---------------------------------------------------------------------------
+// LDS fragment reads.  `row` points at the first element of the operand row
+// (or column, for transposed tiles) inside an LDS tile of TC.
+// ---------------------------------------------------------------------------
+
+// Straight assignment: eight consecutive elements starting at row[8g].
+__device__ __forceinline__ void lds_frag_straight(Frag<__bf16> &f, const __bf16 *row, int g) {
+    f.v = *reinterpret_cast<const bf16x8 *>(row + 8 * g);
+}
+__device__ __forceinline__ void lds_frag_straight(Frag<float> &f, const float *row, int g) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 8 * g);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 8 * g + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+
+// Split assignment over two 16-element halves: row0[4g..4g+3] then row1[4g..4g+3].
+__device__ __forceinline__ void lds_frag_split(Frag<__bf16> &f, const __bf16 *row0, const __bf16 *row1, int g) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(row0 + 4 * g);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(row1 + 4 * g);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+__device__ __forceinline__ void lds_frag_split(Frag<float> &f, const float *row0, const float *row1, int g) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(row0 + 4 * g);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(row1 + 4 * g);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+
+// Build a split-assignment fragment from two accumulator tiles (lane holds
+// rows 4g..4g+3 of each), rounding to the operand type.
+template <typename TC>
+__device__ __forceinline__ void acc_to_frag(Frag<TC> &f, const f32x4 &lo, const f32x4 &hi) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.set(t, lo[t]);
+        f.set(t + 4, hi[t]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Global memory element access for the two storage types.
+// ---------------------------------------------------------------------------
+template <typename TS> struct Store;
+
+template <> struct Store<float> {
+    static constexpr int VEC = 4;  // elements per 16-byte vector
+    __device__ __forceinline__ static float load(const void *p, long i) {
+        return static_cast<const float *>(p)[i];
+    }
+};
+
+template <> struct Store<__bf16> {
+    static constexpr int VEC = 8;
+    __device__ __forceinline__ static float load(const void *p, long i) {
+        return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    }
+};
+
+// Unpack a 16-byte vector of storage elements to floats (VEC of them).
+__device__ __forceinline__ void unpack16(const uint4 &u, float *out, float) {
+    out[0] = __uint_as_float(u.x);
+    out[1] = __uint_as_float(u.y);
+    out[2] = __uint_as_float(u.z);
+    out[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 &u, float *out, __bf16) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+// Sum over the four lane groups (lanes p, p+16, p+32, p+48).
+__device__ __forceinline__ float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+}  // namespace la

@@ -1,0 +1,64 @@
+// la_internal.h -- host-side plumbing between the C ABI (la_api.cpp) and the
+// kernel launchers (la_fwd_dk*.hip, la_decode.hip, la_bwd*.hip).
+#pragma once
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+namespace la {
+
+struct FwdDesc {
+    const void *q, *k, *v;
+    void *o;
+    float *den;
+    const float *S0, *z0;
+    float *S_out, *z_out;
+    int B, H, N, DK, DV, C;
+    int in_bf16, out_bf16;
+    float *ws;
+    hipStream_t stream;
+};
+
+struct DecodeDesc {
+    float *S, *z;
+    const void *q, *k, *v;
+    void *o;
+    int B, H, DK, DV;
+    int in_bf16;
+    hipStream_t stream;
+};
+
+struct BwdDesc {
+    const void *q, *k, *v, *o;
+    const float *den;
+    const void *dO;
+    void *dq, *dk, *dv;
+    int B, H, N, DK, DV, C;
+    int in_bf16;
+    float *ws;
+    hipStream_t stream;
+};
+
+// Split of each (batch, head) sequence into P segments of L tokens (L a
+// multiple of C).  Shared by the workspace queries and the launchers so the
+// two always agree.
+int plan_segments(long BH, int N, int C, int *L);
+
+// Floats per stored state: S (DK x DV) followed by z (DK).
+inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
+
+// Per-(bh, element) pass over the P segment states stored at ws[bh][P][DK*DV + DK]:
+// mode 0 replaces them by their exclusive prefix (S0, z0 folded in when given),
+// mode 1 writes their total into segment slot 0.  Fixed summation order.
+hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
+                           int mode, hipStream_t stream);
+
+hipError_t run_fwd_dk16(const FwdDesc &d, bool causal);
+hipError_t run_fwd_dk32(const FwdDesc &d, bool causal);
+hipError_t run_fwd_dk64(const FwdDesc &d, bool causal);
+hipError_t run_fwd_dk128(const FwdDesc &d, bool causal);
+hipError_t run_decode(const DecodeDesc &d);
+size_t bwd_workspace_bytes(int B, int H, int N, int DK, int DV, int C);
+hipError_t run_bwd(const BwdDesc &d);
+
+}  // namespace la

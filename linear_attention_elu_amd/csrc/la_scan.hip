@@ -1,0 +1,50 @@
+// la_scan.hip -- prefix sums of per-segment states across the segments of one
+// (batch, head).  The causal prefix sums S_i, z_i form a scan, which can be
+// evaluated in parallel (blog digest "Theoretical significance / prefix-sum
+// parallelism"; itwiki table "Comparison of forms", chunked row): segments
+// first reduce their own chunks, this kernel turns the segment totals into the
+// state entering each segment, and the segments then run their chunk loops
+// independently.
+#include <hip/hip_runtime.h>
+
+#include "la_internal.h"
+
+namespace la {
+
+// Prefix over segments, per (bh, element): exclusive prefix (mode 0, the
+// initial state folded in) or total into slot 0 (mode 1).  Fixed order.
+static __global__ void __launch_bounds__(256)
+la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode) {
+    const int SS = DK * DV + DK;
+    const long bh = blockIdx.x;
+    const int idx = blockIdx.y * 256 + threadIdx.x;
+    if (idx >= SS) return;
+    float *base = ws + bh * (long)P * SS + idx;
+    if (mode == 0) {
+        float run = 0.f;
+        if (idx < DK * DV) {
+            if (S0) run = S0[bh * (long)DK * DV + idx];
+        } else if (z0) {
+            run = z0[bh * (long)DK + (idx - DK * DV)];
+        }
+        for (int s = 0; s < P; ++s) {
+            const float a = base[(long)s * SS];
+            base[(long)s * SS] = run;
+            run += a;
+        }
+    } else {
+        float run = 0.f;
+        for (int s = 0; s < P; ++s) run += base[(long)s * SS];
+        base[0] = run;
+    }
+}
+
+hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
+                           int mode, hipStream_t stream) {
+    const long SS = state_floats(DK, DV);
+    const dim3 grid((unsigned)BH, (unsigned)((SS + 255) / 256));
+    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,43 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle runs.
+
+This module draws random numbers and nothing else: it holds none of the
+method's arithmetic.  Inputs are i.i.d. standard normals drawn with
+numpy.random.default_rng(seed) in float32, tensor by tensor in the order
+q, k, v, dO; bf16 inputs are the round-to-nearest-even casts of those float32
+draws (torch's .to(torch.bfloat16)).
+"""
+from __future__ import annotations
+
+from typing import Dict, Sequence, Tuple
+
+import numpy as np
+
+
+def normals(shapes: Sequence[Tuple[int, ...]], seed: int = 0) -> Tuple[np.ndarray, ...]:
+    """Float32 standard normals of the given shapes, drawn in order from one stream."""
+    rng = np.random.default_rng(seed)
+    return tuple(rng.standard_normal(tuple(s), dtype=np.float32) for s in shapes)
+
+
+def attention_inputs(B: int, H: int, N: int, dk: int, dv: int, seed: int = 0,
+                     with_grad: bool = False) -> Dict[str, np.ndarray]:
+    """q, k [B,H,N,dk], v [B,H,N,dv] (and dO [B,H,N,dv]) as float32."""
+    shapes = [(B, H, N, dk), (B, H, N, dk), (B, H, N, dv)]
+    names = ["q", "k", "v"]
+    if with_grad:
+        shapes.append((B, H, N, dv))
+        names.append("dO")
+    return dict(zip(names, normals(shapes, seed)))
+
+
+def decode_inputs(T: int, B: int, H: int, dk: int, dv: int, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Per-step q, k [T,B,H,dk] and v [T,B,H,dv] as float32."""
+    q, k, v = normals([(T, B, H, dk), (T, B, H, dk), (T, B, H, dv)], seed)
+    return {"q": q, "k": k, "v": v}
+
+
+def to_torch(x: np.ndarray, dtype, device):
+    """float32 array -> torch tensor of `dtype` on `device` (bf16 by RNE cast)."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(dtype).contiguous()
