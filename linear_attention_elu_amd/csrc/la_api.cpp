@@ -3,16 +3,16 @@
 // invalid call enqueues nothing.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "la.h"
 #include "la_internal.h"
 
 namespace la {
 
-int plan_segments(long BH, int N, int C, int *L) {
+int plan_segments(long BH, int N, int C, long target_wg, int *L) {
     const long nch = (N + (long)C - 1) / C;
-    // Aim for about four workgroups per compute unit over 256 CUs; never
-    // split a sequence finer than one chunk per segment.
-    const long target_wg = 1024;
+    // Never split a sequence finer than one chunk per segment.
     long want = (target_wg + BH - 1) / BH;
     if (want > nch) want = nch;
     if (want < 1) want = 1;
@@ -20,6 +20,26 @@ int plan_segments(long BH, int N, int C, int *L) {
     const long P = (nch + cps - 1) / cps;
     *L = (int)(cps * C);
     return (int)P;
+}
+
+long resident_workgroups(const void *kernel, int slot) {
+    constexpr int kDevices = 64, kSlots = 96;
+    static std::atomic<long> cache[kDevices][kSlots];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices || slot < 0 || slot >= kSlots) dev = -1;
+    if (dev >= 0) {
+        const long c = cache[dev][slot].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    long n = (long)per_cu * cus;
+    if (n > kMaxTargetWg) n = kMaxTargetWg;
+    if (dev >= 0) cache[dev][slot].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace la
@@ -43,7 +63,7 @@ size_t fwd_ws_bytes(int B, int H, int N, int dk, int dv, int C, bool causal) {
     if (B < 1 || H < 1 || N < 1 || !dim_ok(dk) || !dim_ok(dv) || !chunk_ok(C)) return 0;
     const long BH = (long)B * H;
     int L = 0;
-    const int P = la::plan_segments(BH, N, C, &L);
+    const int P = la::plan_segments(BH, N, C, la::kMaxTargetWg, &L);
     if (causal && P == 1) return 0;
     return (size_t)BH * P * la::state_floats(dk, dv) * sizeof(float);
 }

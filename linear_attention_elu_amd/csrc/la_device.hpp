@@ -134,6 +134,50 @@ __device__ __forceinline__ void lds_frag_split(Frag<float> &f, const float *row0
     }
 }
 
+// Transposed reads of a row-major tile (LDS), for operands whose K index is
+// the tile's row index.  The result slots t = 0..3 of the lane at position p
+// are tile[row0 + t][col0 + p] and slots 4..7 are tile[row1 + t][col0 + p];
+// row0 and row1 must be the same for the 16 lanes of a lane group.
+//
+// bf16: one ds_read_b64_tr_b16 per half.  Inside each group of 16 lanes that
+// instruction hands lane i the element i % 4 of the 8-byte rows fetched by
+// lanes i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12; so lane a fetches row
+// row0 + a / 4 at columns col0 + 4 (a % 4) .. + 3.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_tr4(const __bf16 *tile, int ld, int row0, int col0, int p) {
+    const __bf16 *a = tile + (row0 + (p >> 2)) * ld + col0 + 4 * (p & 3);
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4 *)(a));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ void lds_frag_tr(Frag<__bf16> &f, const __bf16 *tile, int ld, int row0, int row1,
+                                            int col0, int p) {
+    const bf16x4 a = lds_tr4(tile, ld, row0, col0, p);
+    const bf16x4 b = lds_tr4(tile, ld, row1, col0, p);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+
+// fp32 tiles: plain strided reads (the fp32 path is not bandwidth-critical).
+__device__ __forceinline__ void lds_frag_tr(Frag<float> &f, const float *tile, int ld, int row0, int row1,
+                                            int col0, int p) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = tile[(row0 + t) * ld + col0 + p];
+        f.v[t + 4] = tile[(row1 + t) * ld + col0 + p];
+    }
+}
+
+template <typename TC> __device__ __forceinline__ void frag_ones(Frag<TC> &f) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f.set(t, 1.0f);
+}
+
 // Build a split-assignment fragment from two accumulator tiles (lane holds
 // rows 4g..4g+3 of each), rounding to the operand type.
 template <typename TC>

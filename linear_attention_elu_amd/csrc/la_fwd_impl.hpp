@@ -14,11 +14,19 @@
 // (the prefix sum is a scan and can be taken in parallel: blog digest
 // "Theoretical significance / prefix-sum parallelism").
 //
+// Data path of one chunk: the workgroup loads q, k, v rows with 16-byte
+// global loads one chunk ahead into registers, applies phi to q and k while
+// writing the rows to LDS (row-major, 16-byte writes), and every matrix
+// operand is then read from those row-major tiles -- with plain reads where
+// the contraction runs over features and with the gfx950 transpose read
+// (ds_read_b64_tr_b16) where it runs over tokens.
+//
 // Work split inside a workgroup of four waves: wave w owns value-column
 // blocks cb = w, w + 4, ... (16 columns each).  Its slice S[:, cb] of the
 // state lives in accumulator registers for the whole segment and is fed back
 // to the matrix cores as an operand through the split K assignment (see
-// la_device.hpp), so the carry never leaves the registers.  Each wave
+// la_device.hpp), so the carry never leaves the registers; the normaliser z
+// is carried the same way, as phi(K)^T times an all-ones operand.  Each wave
 // computes the transposed score tiles A^T = phi(K) phi(Q)^T itself and the
 // transposed output O^T(cb) = V^T(cb) A^T + S(cb)^T phi(Q)^T, which puts each
 // query's normaliser in the lanes that store that query's outputs.
@@ -45,24 +53,32 @@ struct FwdParams {
     float *seg_out;         // MODE_AGG: per (bh, segment) aggregates
     float *S_fin;           // final state of the last segment (nullable)
     float *z_fin;
-    int N, C, L, P;         // L = tokens per segment (a multiple of C)
+    int N, C;
+    int L;                  // tokens per segment of this launch (a multiple of C)
+    int state_P;            // segments per (bh) in the state array
+    int state_mult;         // segment s of this launch starts at state slot s * state_mult
     int out_bf16;
 };
 
 template <int DK, int DV, typename TC> struct alignas(16) FwdSmem {
     static constexpr int DKP = DK < 32 ? 32 : DK;        // feature dim padded to a K step
     static constexpr int PAD = 16 / sizeof(TC);          // 16-byte row padding
-    static constexpr int LQ = DKP + PAD;                  // row length of sQ, sK
-    static constexpr int LT = kCMax + PAD;                // row length of sKt, sVt
+    static constexpr int LQ = DKP + PAD;                  // row length of q, k tiles
+    static constexpr int LV = DV + PAD;                   // row length of the v tile
     TC q[kCMax * LQ];    // phi(Q) rows
     TC k[kCMax * LQ];    // phi(K) rows
-    TC kt[DK * LT];      // phi(K)^T (feature-major)
-    TC vt[DV * LT];      // V^T (value-column-major)
-    float z[2][DKP];     // normaliser, ping-pong between chunks
+    TC v[kCMax * LV];    // V rows
 };
+
+// Waves per SIMD the compiler must leave room for (registers are split
+// among them): three for the d = 64 bf16 kernels, which are latency-bound.
+template <int DK, int DV, typename TI> constexpr int fwd_waves_per_eu() {
+    return (sizeof(TI) == 2 && DK <= 64 && DV <= 64) ? 3 : 1;
+}
 
 template <int DK, int DV, typename TI, int MODE>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI>())))
 la_chunk_kernel(const FwdParams p) {
     using TC = TI;  // matrix operands keep the input precision
     using SM = FwdSmem<DK, DV, TC>;
@@ -94,6 +110,7 @@ la_chunk_kernel(const FwdParams p) {
     const int nch = (row_end - row_begin + C - 1) / C;
     const int nib = C / 16;                 // query/key row blocks per chunk
     const int nts = (C + 31) / 32;          // token K steps per chunk
+    const bool has_cols = wave < CBT;       // waves without value columns only stage data
 
     const char *qg = static_cast<const char *>(p.q) + (bh * N) * (long)DK * sizeof(TI);
     const char *kg = static_cast<const char *>(p.k) + (bh * N) * (long)DK * sizeof(TI);
@@ -104,14 +121,13 @@ la_chunk_kernel(const FwdParams p) {
         uint32_t *w = reinterpret_cast<uint32_t *>(&sm);
         for (int i = tid; i < (int)(sizeof(SM) / 4); i += kThreads) w[i] = 0u;
     }
-    __syncthreads();
 
     // ---- state entering this segment ----
     const float *Sin = nullptr;
     const float *zin = nullptr;
     if (MODE == MODE_APPLY || MODE == MODE_CAUSAL) {
         if (p.seg_state) {
-            const long slot = (MODE == MODE_APPLY) ? bh * p.P : bh * p.P + seg;
+            const long slot = (MODE == MODE_APPLY) ? bh * p.state_P : bh * p.state_P + (long)seg * p.state_mult;
             Sin = p.seg_state + slot * (long)(DK * DV + DK);
             zin = Sin + DK * DV;
         } else if (p.S0) {
@@ -120,30 +136,44 @@ la_chunk_kernel(const FwdParams p) {
         }
     }
 
+    // S(cb) slices and z in accumulator layout: lane (pp, g) holds rows
+    // 16E + 4g + r; for z every column holds the same value.
     f32x4 accS[CBW][NE];
+    f32x4 accZ[NE];
 #pragma unroll
-    for (int cs = 0; cs < CBW; ++cs)
+    for (int E = 0; E < NE; ++E) {
 #pragma unroll
-        for (int E = 0; E < NE; ++E) {
+        for (int r = 0; r < 4; ++r) accZ[E][r] = zin ? zin[16 * E + 4 * g + r] : 0.0f;
+#pragma unroll
+        for (int cs = 0; cs < CBW; ++cs) {
             const int cb = wave + 4 * cs;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 accS[cs][E][r] = (Sin && cb < CBT) ? Sin[(16 * E + 4 * g + r) * DV + 16 * cb + pp] : 0.0f;
         }
-    if (zin && tid < DK) sm.z[0][tid] = zin[tid];
+    }
 
-    // Operand copy of the state for the inter-chunk read (rounded to TC).
+    // Operand copies of the state for the inter-chunk read (rounded to TC):
+    // S(cb)^T and z as A operands over features in the split assignment (for z
+    // all sixteen operand rows are the same vector).
     Frag<TC> fragS[CBW][NSE];
+    Frag<TC> fragZ[NSE];
     auto refresh_state_frags = [&]() {
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cs = 0; cs < CBW; ++cs)
+        for (int s = 0; s < NSE; ++s) {
 #pragma unroll
-            for (int s = 0; s < NSE; ++s) {
-                const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            for (int cs = 0; cs < CBW; ++cs)
                 acc_to_frag(fragS[cs][s], accS[cs][2 * s], (2 * s + 1 < NE) ? accS[cs][2 * s + 1] : zero4);
-            }
+            acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
+        }
     };
-    refresh_state_frags();
+    if (MODE != MODE_AGG) refresh_state_frags();
+    Frag<TC> ones;
+    frag_ones(ones);
+    bool diag_keep[4];  // causal mask on a diagonal score tile: row 4g + r <= column pp
+#pragma unroll
+    for (int r = 0; r < 4; ++r) diag_keep[r] = 4 * g + r <= pp;
 
     // ---- register prefetch of one chunk ----
     uint4 rq[NEED_Q ? NLQ : 1], rk[NEED_K ? NLQ : 1], rv[NEED_K ? NLV : 1];
@@ -179,159 +209,130 @@ la_chunk_kernel(const FwdParams p) {
     };
 
     // Write the prefetched chunk into LDS, applying phi to q and k (rows at
-    // or beyond nrows, and beyond C, become zeros: they add nothing).
-    auto stage_chunk = [&](int nrows) {
-        if (NEED_Q) {
+    // or beyond nrows become zeros: they add nothing; rows beyond C are never
+    // written and stay zero).  V is copied as loaded.
+    auto stage_phi = [&](const uint4 *regs, int nl, int vpr, TC *tile, int ld, int nrows) {
 #pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const int idx = tid + kThreads * i;
-                const int row = idx / VQ;
-                const int col = (idx % VQ) * VEC;
-                if (row < C) {
-                    float x[VEC];
-                    unpack16(rq[i], x, TI());
+        for (int i = 0; i < nl; ++i) {
+            const int idx = tid + kThreads * i;
+            const int row = idx / vpr;
+            const int col = (idx % vpr) * VEC;
+            if (row < C) {
+                float x[VEC];
+                unpack16(regs[i], x, TI());
+                Frag<TC> w;  // VEC <= 8 elements, written as one 16-byte store
+                if (nrows == C) {
 #pragma unroll
-                    for (int t = 0; t < VEC; ++t) {
-                        const float y = row < nrows ? to_operand<TC>(phi(x[t])) : 0.0f;
-                        sm.q[row * SM::LQ + col + t] = static_cast<TC>(y);
-                    }
+                    for (int t = 0; t < VEC; ++t) w.set(t, phi(x[t]));
+                } else {
+#pragma unroll
+                    for (int t = 0; t < VEC; ++t) w.set(t, row < nrows ? phi(x[t]) : 0.0f);
                 }
-            }
-        }
-        if (NEED_K) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const int idx = tid + kThreads * i;
-                const int row = idx / VQ;
-                const int col = (idx % VQ) * VEC;
-                if (row < C) {
-                    float x[VEC];
-                    unpack16(rk[i], x, TI());
-#pragma unroll
-                    for (int t = 0; t < VEC; ++t) {
-                        const TC y = static_cast<TC>(row < nrows ? phi(x[t]) : 0.0f);
-                        if (MODE == MODE_CAUSAL) sm.k[row * SM::LQ + col + t] = y;
-                        sm.kt[(col + t) * SM::LT + row] = y;
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NLV; ++i) {
-                const int idx = tid + kThreads * i;
-                const int row = idx / VV;
-                const int col = (idx % VV) * VEC;
-                if (row < C) {
-                    float x[VEC];
-                    unpack16(rv[i], x, TI());
-#pragma unroll
-                    for (int t = 0; t < VEC; ++t)
-                        sm.vt[(col + t) * SM::LT + row] = static_cast<TC>(row < nrows ? x[t] : 0.0f);
+                if constexpr (sizeof(TC) == 2) {
+                    *reinterpret_cast<uint4 *>(tile + row * ld + col) = __builtin_bit_cast(uint4, w.v);
+                } else {
+                    f32x4 w4 = {w.get(0), w.get(1), w.get(2), w.get(3)};
+                    *reinterpret_cast<f32x4 *>(tile + row * ld + col) = w4;
                 }
             }
         }
     };
-
-    float zreg[2] = {0.f, 0.f};  // wave 0: running z for features lane, lane + 64
-    if (wave == 0) {
-        if (lane < DK) zreg[0] = zin ? zin[lane] : 0.0f;
-        if (lane + 64 < DK) zreg[1] = zin ? zin[lane + 64] : 0.0f;
-    }
+    auto stage_raw = [&](const uint4 *regs, int nl, int vpr, TC *tile, int ld) {
+#pragma unroll
+        for (int i = 0; i < nl; ++i) {
+            const int idx = tid + kThreads * i;
+            const int row = idx / vpr;
+            if (row < C)  // rows past nrows were loaded as zeros
+                *reinterpret_cast<uint4 *>(tile + row * ld + (idx % vpr) * VEC) = regs[i];
+        }
+    };
 
     if (nch > 0) load_chunk(row_begin, min(C, row_end - row_begin));
 
     for (int ch = 0; ch < nch; ++ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        const int zc = (MODE == MODE_APPLY) ? 0 : (ch & 1);
-        __syncthreads();  // previous chunk's LDS reads are done
-        stage_chunk(nrows);
+        __syncthreads();  // previous chunk's LDS reads are done (and the initial fill)
+        if (NEED_Q) stage_phi(rq, NLQ, VQ, sm.q, SM::LQ, nrows);
+        if (NEED_K) {
+            stage_phi(rk, NLQ, VQ, sm.k, SM::LQ, nrows);
+            stage_raw(rv, NLV, VV, sm.v, SM::LV);
+        }
         if (ch + 1 < nch) {
             const int r1 = r0 + C;
             load_chunk(r1, min(C, row_end - r1));
         }
         __syncthreads();  // chunk tiles ready
 
-        // ---- normaliser carry (wave 0): z_next = z + sum of this chunk's phi(k) ----
-        if (NEED_K && wave == 0) {
+        if (NEED_Q && has_cols) {
+            // V^T(cb) in the split assignment over tokens (A operand of the intra product)
+            Frag<TC> fvt[CBW][2];
+            if (MODE == MODE_CAUSAL) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int e = lane + 64 * h;
-                if (e < DK) {
-                    float s = 0.f;
-                    const TC *row = &sm.kt[e * SM::LT];
-                    for (int j = 0; j < kCMax; ++j) s += static_cast<float>(row[j]);
-                    zreg[h] += s;
-                    sm.z[zc ^ 1][e] = zreg[h];
-                }
+                for (int cs = 0; cs < CBW; ++cs)
+#pragma unroll
+                    for (int jp = 0; jp < 2; ++jp)
+                        if (2 * jp < nib)
+                            lds_frag_tr(fvt[cs][jp], sm.v, SM::LV, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g,
+                                        16 * (wave + 4 * cs), pp);
             }
-        }
-
-        if (NEED_Q && wave < CBT) {
-            const float *zcur = sm.z[zc];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 if (I < nib) {
                     const TC *qrow = &sm.q[(16 * I + pp) * SM::LQ];
-                    Frag<TC> fqs[NSE], fqp[NSE];
-                    float part = 0.f;
+                    Frag<TC> fq[NSE];
 #pragma unroll
-                    for (int s = 0; s < NSE; ++s) {
-                        lds_frag_straight(fqs[s], qrow + 32 * s, g);
-                        lds_frag_split(fqp[s], qrow + 32 * s, qrow + 32 * s + 16, g);
+                    for (int s = 0; s < NSE; ++s) lds_frag_split(fq[s], qrow + 32 * s, qrow + 32 * s + 16, g);
+                    // den_i = phi(q_i) . z + sum_{j <= i} A_ij, both on the matrix
+                    // cores: every accumulator slot of lane (i, g) ends up holding den_i.
+                    f32x4 accD = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            part += fqp[s].get(t) * zcur[32 * s + 4 * g + t];
-                            part += fqp[s].get(t + 4) * zcur[32 * s + 16 + 4 * g + t];
-                        }
-                    }
-                    f32x4 accA[4];
+                    for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
+                    Frag<TC> fb[2];  // A^T key-block pairs as B operands (split over tokens)
                     if (MODE == MODE_CAUSAL) {
+                        f32x4 accA[4];
 #pragma unroll
                         for (int J = 0; J < 4; ++J) {
                             accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
                             if (J <= I) {
-                                const TC *krow = &sm.k[(16 * J + pp) * SM::LQ];
 #pragma unroll
                                 for (int s = 0; s < NSE; ++s) {
+                                    // phi(K) rows of key block J, split over features
                                     Frag<TC> fk;
-                                    lds_frag_straight(fk, krow + 32 * s, g);
-                                    accA[J] = mma(fk, fqs[s], accA[J]);
-                                }
-#pragma unroll
-                                for (int r = 0; r < 4; ++r) {
-                                    float a = to_operand<TC>(accA[J][r]);
-                                    if (J == I && 4 * g + r > pp) a = 0.f;  // causal mask j <= i
-                                    accA[J][r] = a;
-                                    part += a;
+                                    const TC *krow = &sm.k[(16 * J + pp) * SM::LQ + 32 * s];
+                                    lds_frag_split(fk, krow, krow + 16, g);
+                                    accA[J] = mma(fk, fq[s], accA[J]);
                                 }
                             }
                         }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) accA[I][r] = diag_keep[r] ? accA[I][r] : 0.f;  // j <= i
+#pragma unroll
+                        for (int jp = 0; jp < 2; ++jp) {
+                            if (2 * jp <= I) {
+                                acc_to_frag(fb[jp], accA[2 * jp], accA[2 * jp + 1]);
+                                accD = mma(ones, fb[jp], accD);
+                            }
+                        }
                     }
-                    const float den = sum_over_groups(part);
+                    const float den = accD[0];
                     const int row_local = 16 * I + pp;
                     const bool valid = row_local < nrows;
                     const long grow = (long)r0 + row_local;
                     if (p.den && wave == 0 && g == 0 && valid) p.den[bh * N + grow] = den;
-                    const float inv = 1.0f / den;
+                    const float inv = __builtin_amdgcn_rcpf(den);
 #pragma unroll
                     for (int cs = 0; cs < CBW; ++cs) {
                         const int cb = wave + 4 * cs;
                         if (cb < CBT) {
                             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                             if (MODE == MODE_CAUSAL) {
-                                const TC *vrow = &sm.vt[(16 * cb + pp) * SM::LT];
 #pragma unroll
-                                for (int J0 = 0; J0 < 4; J0 += 2) {
-                                    if (J0 <= I) {
-                                        Frag<TC> fa, fb;
-                                        lds_frag_split(fa, vrow + 16 * J0, vrow + 16 * J0 + 16, g);
-                                        acc_to_frag(fb, accA[J0], accA[J0 + 1]);
-                                        acc = mma(fa, fb, acc);
-                                    }
-                                }
+                                for (int jp = 0; jp < 2; ++jp)
+                                    if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
                             }
 #pragma unroll
-                            for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fqp[s], acc);
+                            for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
                             if (valid) {
                                 const long base = (bh * N + grow) * DV + 16 * cb + 4 * g;
                                 if (p.out_bf16) {
@@ -352,24 +353,25 @@ la_chunk_kernel(const FwdParams p) {
             }
         }
 
-        // ---- state carry: S(cb) += phi(K_c)^T V_c(cb) ----
-        if (NEED_K) {
+        // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
+        if (NEED_K && has_cols) {
 #pragma unroll
-            for (int cs = 0; cs < CBW; ++cs) {
-                const int cb = wave + 4 * cs;
-                if (cb < CBT) {
-                    const TC *vrow = &sm.vt[(16 * cb + pp) * SM::LT];
+            for (int s = 0; s < 2; ++s) {
+                if (s < nts) {
+                    Frag<TC> fkt[NE];
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        if (s < nts) {
+                    for (int E = 0; E < NE; ++E) {
+                        lds_frag_tr(fkt[E], sm.k, SM::LQ, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * E, pp);
+                        accZ[E] = mma(fkt[E], ones, accZ[E]);
+                    }
+#pragma unroll
+                    for (int cs = 0; cs < CBW; ++cs) {
+                        const int cb = wave + 4 * cs;
+                        if (cb < CBT) {
                             Frag<TC> fv;
-                            lds_frag_straight(fv, vrow + 32 * s, g);
+                            lds_frag_tr(fv, sm.v, SM::LV, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * cb, pp);
 #pragma unroll
-                            for (int E = 0; E < NE; ++E) {
-                                Frag<TC> fk;
-                                lds_frag_straight(fk, &sm.kt[(16 * E + pp) * SM::LT + 32 * s], g);
-                                accS[cs][E] = mma(fk, fv, accS[cs][E]);
-                            }
+                            for (int E = 0; E < NE; ++E) accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
                         }
                     }
                 }
@@ -382,13 +384,13 @@ la_chunk_kernel(const FwdParams p) {
     float *Sdst = nullptr;
     float *zdst = nullptr;
     if (MODE == MODE_AGG) {
-        Sdst = p.seg_out + (bh * p.P + seg) * (long)(DK * DV + DK);
+        Sdst = p.seg_out + (bh * p.state_P + seg) * (long)(DK * DV + DK);
         zdst = Sdst + DK * DV;
-    } else if (MODE == MODE_CAUSAL && seg == p.P - 1 && p.S_fin) {
+    } else if (MODE == MODE_CAUSAL && seg == (int)gridDim.y - 1 && p.S_fin) {
         Sdst = p.S_fin + bh * (long)(DK * DV);
         zdst = p.z_fin + bh * (long)DK;
     }
-    if (Sdst) {
+    if (Sdst && has_cols) {
 #pragma unroll
         for (int cs = 0; cs < CBW; ++cs) {
             const int cb = wave + 4 * cs;
@@ -400,9 +402,11 @@ la_chunk_kernel(const FwdParams p) {
                         Sdst[(16 * E + 4 * g + r) * DV + 16 * cb + pp] = accS[cs][E][r];
             }
         }
-        if (wave == 0) {
-            if (lane < DK) zdst[lane] = zreg[0];
-            if (lane + 64 < DK) zdst[lane + 64] = zreg[1];
+        if (wave == 0 && pp == 0) {
+#pragma unroll
+            for (int E = 0; E < NE; ++E)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zdst[16 * E + 4 * g + r] = accZ[E][r];
         }
     }
 }

@@ -13,8 +13,20 @@ namespace la {
 template <int DK, int DV, typename TI>
 hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    int L = 0;
-    const int P = plan_segments(BH, d.N, d.C, &L);
+    const int kslot = ((DK == 16 ? 0 : DK == 32 ? 1 : DK == 64 ? 2 : 3) * 4 +
+                       (DV == 16 ? 0 : DV == 32 ? 1 : DV == 64 ? 2 : 3)) * 2 + (sizeof(TI) == 2);
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG>;
+    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL> : &la_chunk_kernel<DK, DV, TI, MODE_APPLY>;
+    // Each launch aims at one round of resident workgroups.  The aggregate
+    // pass uses fine segments; a causal segment is a run of `mult` of them.
+    const long target_agg = resident_workgroups(reinterpret_cast<const void *>(agg_kernel), kslot * 3 + MODE_AGG);
+    const long target_main = resident_workgroups(reinterpret_cast<const void *>(main_kernel),
+                                                 kslot * 3 + (causal ? MODE_CAUSAL : MODE_APPLY));
+    int Lf = 0;
+    const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
+    const long want_main = (target_main + BH - 1) / BH;
+    const int mult = (int)((Pf + want_main - 1) / want_main);
+    const int Pm = (Pf + mult - 1) / mult;
 
     FwdParams p{};
     p.q = d.q;
@@ -24,38 +36,47 @@ hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     p.den = d.den;
     p.N = d.N;
     p.C = d.C;
-    p.L = L;
-    p.P = P;
     p.out_bf16 = d.out_bf16;
-
-    const dim3 grid((unsigned)BH, (unsigned)P);
+    p.state_P = Pf;
     hipError_t err;
 
     if (causal) {
         p.S_fin = d.S_out;
         p.z_fin = d.z_out;
-        if (P > 1) {
+        if (Pm > 1) {
             p.seg_out = d.ws;
-            la_chunk_kernel<DK, DV, TI, MODE_AGG><<<grid, kThreads, 0, d.stream>>>(p);
+            p.L = Lf;
+            p.state_mult = 1;
+            agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
-            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, P, DK, DV, 0, d.stream)) != hipSuccess) return err;
+            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
             p.seg_state = d.ws;
+            p.state_mult = mult;
+            p.L = Lf * mult;
+            main_kernel<<<dim3((unsigned)BH, (unsigned)Pm), kThreads, 0, d.stream>>>(p);
         } else {
             p.S0 = d.S0;
             p.z0 = d.z0;
+            p.L = d.N;
+            main_kernel<<<dim3((unsigned)BH, 1u), kThreads, 0, d.stream>>>(p);
         }
-        la_chunk_kernel<DK, DV, TI, MODE_CAUSAL><<<grid, kThreads, 0, d.stream>>>(p);
         return hipGetLastError();
     }
 
     p.seg_out = d.ws;
-    la_chunk_kernel<DK, DV, TI, MODE_AGG><<<grid, kThreads, 0, d.stream>>>(p);
+    p.L = Lf;
+    p.state_mult = 1;
+    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (P > 1) {
-        if ((err = launch_seg_scan(d.ws, nullptr, nullptr, BH, P, DK, DV, 1, d.stream)) != hipSuccess) return err;
+    if (Pf > 1) {
+        if ((err = launch_seg_scan(d.ws, nullptr, nullptr, BH, Pf, DK, DV, 1, d.stream)) != hipSuccess) return err;
     }
+    // The read-out is independent per row: split it on its own.
+    int La = 0;
+    const int Pa = plan_segments(BH, d.N, d.C, target_main, &La);
     p.seg_state = d.ws;
-    la_chunk_kernel<DK, DV, TI, MODE_APPLY><<<grid, kThreads, 0, d.stream>>>(p);
+    p.L = La;
+    main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), kThreads, 0, d.stream>>>(p);
     return hipGetLastError();
 }
 

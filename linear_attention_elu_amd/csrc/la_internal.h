@@ -40,9 +40,17 @@ struct BwdDesc {
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a
-// multiple of C).  Shared by the workspace queries and the launchers so the
-// two always agree.
-int plan_segments(long BH, int N, int C, int *L);
+// multiple of C), aiming at `target_wg` workgroups in total.  P never
+// decreases when target_wg grows, so the workspace queries size for
+// kMaxTargetWg and the launchers, which aim at what the GPU holds resident
+// at once (never more than kMaxTargetWg), always fit.
+constexpr long kMaxTargetWg = 2048;
+int plan_segments(long BH, int N, int C, long target_wg, int *L);
+
+// Workgroups of `kernel` (256 threads) the current device keeps resident at
+// once: occupancy per CU times the CU count, at most kMaxTargetWg.  Cached per
+// device and per `slot` (0..95), which must identify the kernel.
+long resident_workgroups(const void *kernel, int slot);
 
 // Floats per stored state: S (DK x DV) followed by z (DK).
 inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
