@@ -185,9 +185,9 @@ def bench_bwd(dev, steps=10, warmup=3, B=8, H=16, N=8192, d=128, C=64, seed=0):
     try:
         wsb = torch.empty(max(1, la.la_bwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
         dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
-        bwd_ms = time_calls(lambda: la.la_bwd_causal(q, k, v, o, den, dO, dq=dq, dk=dk, dv=dv, C=C, ws=wsb),
+        bwd_ms = time_calls(lambda: la.la_bwd_causal(q, k, v, dO, dq=dq, dk=dk, dv=dv, C=C, ws=wsb),
                             steps, warmup, stream)
-        bwd_bytes = B * H * N * (8 * d * 2 + 4)  # q k v o dO den read; dq dk dv written
+        bwd_bytes = B * H * N * 7 * d * 2  # q k v dO read; dq dk dv written
         res.update({"bwd_us": round(bwd_ms * 1e3, 2), "bwd_GBs": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
                     "bwd_hbm_frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
     except la.LAError as e:

@@ -96,8 +96,7 @@ la_status la_fwd_noncausal(const void *q, const void *k, const void *v, void *o,
  *   o_i = phi(q_i)^T S_i / den_i,  den_i = phi(q_i)^T z_i,
  *   S_i = sum_{j<=i} phi(k_j) v_j^T,  z_i = sum_{j<=i} phi(k_j).
  * The result does not depend on C (the chunked form is an exact rewrite);
- * C only sets the tiling.  den (nullable, fp32 [B][H][N]) receives den_i,
- * which la_bwd_causal needs.
+ * C only sets the tiling.  den (nullable, fp32 [B][H][N]) receives den_i.
  */
 la_status la_fwd_causal(const void *q, const void *k, const void *v, void *o, float *den,
                         int B, int H, int N, int d_k, int d_v, int C,
@@ -121,19 +120,22 @@ la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void 
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Causal backward by cumulative sums (exact gradient of la_fwd_causal).
- * With g_i = dO_i, gh_i = g_i / den_i and eps_i = -(g_i . o_i) / den_i:
- *   dphi(q_i) = S_i gh_i + eps_i z_i                (forward prefix sums)
+ * Causal backward by cumulative sums: the exact gradient of la_fwd_causal
+ * with respect to q, k and v for an upstream gradient dO.
+ * With g_i = dO_i, den_i = phi(q_i) . z_i, gh_i = g_i / den_i and
+ * eps_i = -(g_i . o_i) / den_i:
+ *   dphi(q_i) = S_i gh_i + eps_i z_i                   (forward prefix sums)
  *   dphi(k_j) = R_j v_j + r_j,  dv_j = R_j^T phi(k_j)  (reverse suffix sums)
  *   with R_j = sum_{i>=j} phi(q_i) gh_i^T, r_j = sum_{i>=j} phi(q_i) eps_i,
  *   then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).
- * Inputs: q, k, v, o (as produced by la_fwd_causal, storage type `in`), den
- * (fp32, from la_fwd_causal), dO [B][H][N][d_v].  Outputs dq, dk
+ * The forward's outputs are not inputs: den_i and the products with o_i are
+ * recomputed from the prefix sums inside the dq sweep.
+ * Inputs q, k [B][H][N][d_k], v, dO [B][H][N][d_v] in `in`; outputs dq, dk
  * [B][H][N][d_k] and dv [B][H][N][d_v] in `in`.  No per-token state is
- * stored; workspace holds per-segment d_k x (d_v + 1) sums.
+ * stored: the workspace (always required) holds two floats per token and
+ * per-segment d_k x (d_v + 1) prefix and suffix sums.
  */
-la_status la_bwd_causal(const void *q, const void *k, const void *v, const void *o,
-                        const float *den, const void *dO,
+la_status la_bwd_causal(const void *q, const void *k, const void *v, const void *dO,
                         void *dq, void *dk, void *dv,
                         int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
                         void *ws, size_t ws_bytes, hipStream_t stream);

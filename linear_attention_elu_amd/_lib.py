@@ -67,7 +67,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_fwd_causal.restype = i
     lib.la_fwd_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_fwd_causal_state.restype = i
-    lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_causal.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i

@@ -146,22 +146,22 @@ def la_fwd_noncausal(q, k, v, o=None, out_dtype=None, ws=None, stream=None):
     return o
 
 
-def la_bwd_causal(q, k, v, o, den, dO, dq=None, dk=None, dv=None, C: int = 64, ws=None, stream=None):
-    """Cumulative-sum backward.  Returns (dq, dk, dv) in the dtype of q."""
+def la_bwd_causal(q, k, v, dO, dq=None, dk=None, dv=None, C: int = 64, ws=None, stream=None):
+    """Cumulative-sum backward of the causal forward.  Returns (dq, dk, dv) in the dtype of q."""
     B, H, N, d_k, d_v = _shapes(q, k, v)
-    dev = _dev(q, k, v, o, den, dO, dq, dk, dv, ws)
-    if tuple(o.shape) != (B, H, N, d_v) or tuple(dO.shape) != (B, H, N, d_v) or tuple(den.shape) != (B, H, N):
-        raise ValueError("o, dO must be [B,H,N,d_v] and den [B,H,N]")
-    if o.dtype != q.dtype or dO.dtype != q.dtype or den.dtype != torch.float32:
-        raise TypeError("o and dO share the dtype of q; den is float32")
+    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
+    if tuple(dO.shape) != (B, H, N, d_v) or dO.dtype != q.dtype:
+        raise ValueError("dO must be [B,H,N,d_v] in the dtype of q")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("dq, dk, dv must match q, k, v in shape and dtype")
     _dev(dq, dk, dv)
     wp, wb = _ws(la_bwd_causal_workspace_bytes(B, H, N, d_k, d_v, C), dev, ws)
-    rc = _lib.load().la_bwd_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(dO),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d_k, d_v, C, _code(q),
-                                   wp, wb, _stream(dev, stream))
+    rc = _lib.load().la_bwd_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                                   B, H, N, d_k, d_v, C, _code(q), wp, wb, _stream(dev, stream))
     _lib.check(rc, "la_bwd_causal")
     return dq, dk, dv
 

@@ -27,6 +27,10 @@ SOURCES = [
     "la_fwd_dk32.hip",
     "la_fwd_dk64.hip",
     "la_fwd_dk128.hip",
+    "la_bwd_dk16.hip",
+    "la_bwd_dk32.hip",
+    "la_bwd_dk64.hip",
+    "la_bwd_dk128.hip",
 ]
 
 FLAGS = [

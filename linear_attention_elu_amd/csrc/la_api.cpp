@@ -22,8 +22,8 @@ int plan_segments(long BH, int N, int C, long target_wg, int *L) {
     return (int)P;
 }
 
-long resident_workgroups(const void *kernel, int slot) {
-    constexpr int kDevices = 64, kSlots = 96;
+long resident_workgroups(const void *kernel, int slot, int threads) {
+    constexpr int kDevices = 64, kSlots = 160;
     static std::atomic<long> cache[kDevices][kSlots];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices || slot < 0 || slot >= kSlots) dev = -1;
@@ -32,7 +32,7 @@ long resident_workgroups(const void *kernel, int slot) {
         if (c > 0) return c;
     }
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
         cus < 1)
         cus = 256;
@@ -166,23 +166,21 @@ la_status la_fwd_noncausal(const void *q, const void *k, const void *v, void *o,
     return run_fwd(d, false);
 }
 
-la_status la_bwd_causal(const void *q, const void *k, const void *v, const void *o,
-                        const float *den, const void *dO,
+la_status la_bwd_causal(const void *q, const void *k, const void *v, const void *dO,
                         void *dq, void *dk, void *dv,
                         int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
                         void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (!q || !k || !v || !o || !den || !dO || !dq || !dk || !dv) return LA_ERR_NULL_PTR;
+    if (!q || !k || !v || !dO || !dq || !dk || !dv) return LA_ERR_NULL_PTR;
     la_status st = check_shape(B, H, N);
     if (st != LA_OK) return st;
     if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return LA_ERR_UNSUPPORTED;
     if (!dtype_ok(in)) return LA_ERR_BAD_DTYPE;
-    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned(den) || !aligned(dO) ||
-        !aligned(dq) || !aligned(dk) || !aligned(dv) || !aligned_or_null(ws))
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(dO) || !aligned(dq) || !aligned(dk) ||
+        !aligned(dv) || !aligned_or_null(ws))
         return LA_ERR_ALIGNMENT;
     const size_t need = la::bwd_workspace_bytes(B, H, N, d_k, d_v, C);
-    if (need > 0 && (ws == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
-    la::BwdDesc d{q, k, v, o, den, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in == LA_BF16,
-                  static_cast<float *>(ws), stream};
+    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream};
     return from_hip(la::run_bwd(d));
 }
 

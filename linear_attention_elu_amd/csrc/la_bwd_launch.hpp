@@ -1,0 +1,127 @@
+// la_bwd_launch.hpp -- host launch sequence of the cumulative-sum backward.
+//
+//   [P > 1]     aggregates of phi(K)^T V, phi(K)^T 1 per segment -> exclusive prefix
+//   dq sweep    forward over the chunks of every segment; leaves 1/den and eps
+//   [P > 1]     aggregates of (phi(Q)/den)^T dO, (phi(Q)/den)^T e -> exclusive suffix
+//   dk/dv sweep backward over the chunks of every segment
+#pragma once
+
+#include "la_bwd_impl.hpp"
+#include "la_fwd_impl.hpp"
+#include "la_internal.h"
+
+namespace la {
+
+inline size_t bwd_align(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct BwdLayout {
+    size_t inv_den, eps, pre, suf, total;
+};
+
+inline BwdLayout bwd_layout(long BH, int N, int DK, int DV, int Pmax) {
+    BwdLayout l{};
+    l.inv_den = 0;
+    l.eps = bwd_align(l.inv_den + (size_t)BH * N * sizeof(float));
+    l.pre = bwd_align(l.eps + (size_t)BH * N * sizeof(float));
+    const size_t st = (size_t)BH * Pmax * state_floats(DK, DV) * sizeof(float);
+    l.suf = bwd_align(l.pre + st);
+    l.total = bwd_align(l.suf + st);
+    return l;
+}
+
+template <int DK, int DV, typename TI>
+hipError_t run_bwd_t(const BwdDesc &d) {
+    const long BH = (long)d.B * d.H;
+    int Lmax = 0;
+    const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);
+    const BwdLayout lay = bwd_layout(BH, d.N, DK, DV, Pmax);
+    char *ws = reinterpret_cast<char *>(d.ws);
+    float *inv_den = reinterpret_cast<float *>(ws + lay.inv_den);
+    float *eps = reinterpret_cast<float *>(ws + lay.eps);
+    float *pre = reinterpret_cast<float *>(ws + lay.pre);
+    float *suf = reinterpret_cast<float *>(ws + lay.suf);
+    hipError_t err;
+
+    const int kslot = ((DK == 16 ? 0 : DK == 32 ? 1 : DK == 64 ? 2 : 3) * 4 +
+                       (DV == 16 ? 0 : DV == 32 ? 1 : DV == 64 ? 2 : 3)) * 2 + (sizeof(TI) == 2);
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG>;
+    auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI>;
+    auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI>;
+    const long target_agg = resident_workgroups(reinterpret_cast<const void *>(agg_kernel), kslot * 3 + MODE_AGG);
+    const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), 96 + kslot * 2, kBwdThreads);
+    const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), 96 + kslot * 2 + 1, kBwdThreads);
+    int Lf = 0;
+    const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
+    auto split = [&](long target, int *mult) {
+        const long want = (target + BH - 1) / BH;
+        *mult = (int)((Pf + want - 1) / want);
+        return (Pf + *mult - 1) / *mult;
+    };
+    int mult_q = 1, mult_kv = 1;
+    const int Pq = split(target_dq, &mult_q);
+    const int Pkv = split(target_kv, &mult_kv);
+
+    FwdParams a{};
+    a.N = d.N;
+    a.C = d.C;
+    a.L = Lf;
+    a.state_P = Pf;
+    a.state_mult = 1;
+    if (Pq > 1) {
+        a.k = d.k;
+        a.v = d.v;
+        a.seg_out = pre;
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
+    }
+
+    BwdParams b{};
+    b.q = d.q;
+    b.k = d.k;
+    b.v = d.v;
+    b.g = d.dO;
+    b.inv_den = inv_den;
+    b.eps = eps;
+    b.dq = d.dq;
+    b.dk = d.dk;
+    b.dv = d.dv;
+    b.N = d.N;
+    b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
+    b.state_P = Pf;
+
+    b.state = Pq > 1 ? pre : nullptr;
+    b.state_mult = mult_q;
+    b.L = Pq > 1 ? Lf * mult_q : d.N;
+    dq_kernel<<<dim3((unsigned)BH, (unsigned)(Pq > 1 ? Pq : 1)), kBwdThreads, 0, d.stream>>>(b);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    if (Pkv > 1) {
+        a.k = d.q;  // (a phi(Q))^T dO and (a phi(Q))^T e, a = 1 / den
+        a.v = d.dO;
+        a.kscale = inv_den;
+        a.zw = eps;
+        a.seg_out = suf;
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(a);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, d.stream)) != hipSuccess) return err;
+    }
+    b.state = Pkv > 1 ? suf : nullptr;
+    b.state_mult = mult_kv;
+    b.L = Pkv > 1 ? Lf * mult_kv : d.N;
+    dkdv_kernel<<<dim3((unsigned)BH, (unsigned)(Pkv > 1 ? Pkv : 1)), kBwdThreads, 0, d.stream>>>(b);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t run_bwd_dk(const BwdDesc &d) {
+    switch (d.DV) {
+        case 16: return d.in_bf16 ? run_bwd_t<DK, 16, __bf16>(d) : run_bwd_t<DK, 16, float>(d);
+        case 32: return d.in_bf16 ? run_bwd_t<DK, 32, __bf16>(d) : run_bwd_t<DK, 32, float>(d);
+        case 64: return d.in_bf16 ? run_bwd_t<DK, 64, __bf16>(d) : run_bwd_t<DK, 64, float>(d);
+        case 128: return d.in_bf16 ? run_bwd_t<DK, 128, __bf16>(d) : run_bwd_t<DK, 128, float>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace la

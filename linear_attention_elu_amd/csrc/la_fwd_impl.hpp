@@ -51,6 +51,8 @@ struct FwdParams {
     const float *S0;        // per-bh initial state, used only when seg_state is null
     const float *z0;
     float *seg_out;         // MODE_AGG: per (bh, segment) aggregates
+    const float *zw;        // MODE_AGG: per-token weights [BH][N] for z (null: all ones)
+    const float *kscale;    // MODE_AGG: per-token factors [BH][N] applied to phi(k) rows (null: none)
     float *S_fin;           // final state of the last segment (nullable)
     float *z_fin;
     int N, C;
@@ -68,6 +70,8 @@ template <int DK, int DV, typename TC> struct alignas(16) FwdSmem {
     TC q[kCMax * LQ];    // phi(Q) rows
     TC k[kCMax * LQ];    // phi(K) rows
     TC v[kCMax * LV];    // V rows
+    float w[kCMax];      // per-token z weights (MODE_AGG with zw)
+    float s[kCMax];      // per-token phi(k) factors (MODE_AGG with kscale)
 };
 
 // Waves per SIMD the compiler must leave room for (registers are split
@@ -177,7 +181,12 @@ la_chunk_kernel(const FwdParams p) {
 
     // ---- register prefetch of one chunk ----
     uint4 rq[NEED_Q ? NLQ : 1], rk[NEED_K ? NLQ : 1], rv[NEED_K ? NLV : 1];
+    float rw = 0.f, rs = 1.f;
+    const bool weighted = MODE == MODE_AGG && p.zw != nullptr;
+    const bool kscaled = MODE == MODE_AGG && p.kscale != nullptr;
     auto load_chunk = [&](int r0, int nrows) {
+        if (weighted) rw = tid < nrows ? p.zw[bh * N + r0 + tid] : 0.f;
+        if (kscaled) rs = tid < nrows ? p.kscale[bh * N + r0 + tid] : 0.f;
         if (NEED_Q) {
 #pragma unroll
             for (int i = 0; i < NLQ; ++i) {
@@ -237,6 +246,28 @@ la_chunk_kernel(const FwdParams p) {
             }
         }
     };
+    auto stage_phi_scaled = [&](const uint4 *regs, int nl, int vpr, TC *tile, int ld) {
+#pragma unroll
+        for (int i = 0; i < nl; ++i) {
+            const int idx = tid + kThreads * i;
+            const int row = idx / vpr;
+            const int col = (idx % vpr) * VEC;
+            if (row < C) {
+                float x[VEC];
+                unpack16(regs[i], x, TI());
+                const float f = sm.s[row];  // zero past nrows
+                Frag<TC> w;
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) w.set(t, phi(x[t]) * f);
+                if constexpr (sizeof(TC) == 2) {
+                    *reinterpret_cast<uint4 *>(tile + row * ld + col) = __builtin_bit_cast(uint4, w.v);
+                } else {
+                    f32x4 w4 = {w.get(0), w.get(1), w.get(2), w.get(3)};
+                    *reinterpret_cast<f32x4 *>(tile + row * ld + col) = w4;
+                }
+            }
+        }
+    };
     auto stage_raw = [&](const uint4 *regs, int nl, int vpr, TC *tile, int ld) {
 #pragma unroll
         for (int i = 0; i < nl; ++i) {
@@ -255,7 +286,14 @@ la_chunk_kernel(const FwdParams p) {
         __syncthreads();  // previous chunk's LDS reads are done (and the initial fill)
         if (NEED_Q) stage_phi(rq, NLQ, VQ, sm.q, SM::LQ, nrows);
         if (NEED_K) {
-            stage_phi(rk, NLQ, VQ, sm.k, SM::LQ, nrows);
+            if (kscaled) {
+                if (tid < kCMax) sm.s[tid] = rs;  // rows past nrows load 0
+                __syncthreads();
+                stage_phi_scaled(rk, NLQ, VQ, sm.k, SM::LQ);
+            } else {
+                stage_phi(rk, NLQ, VQ, sm.k, SM::LQ, nrows);
+            }
+            if (weighted && tid < kCMax) sm.w[tid] = rw;  // rows past nrows load 0
             stage_raw(rv, NLV, VV, sm.v, SM::LV);
         }
         if (ch + 1 < nch) {
@@ -359,10 +397,22 @@ la_chunk_kernel(const FwdParams p) {
             for (int s = 0; s < 2; ++s) {
                 if (s < nts) {
                     Frag<TC> fkt[NE];
+                    // z weights over this step's tokens (straight assignment), as a
+                    // value and its rounding remainder when the operands are bf16
+                    Frag<TC> fw = ones, fw_lo;
+                    if (weighted) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            const float x = sm.w[32 * s + 8 * g + t];
+                            fw.set(t, x);
+                            fw_lo.set(t, x - fw.get(t));
+                        }
+                    }
 #pragma unroll
                     for (int E = 0; E < NE; ++E) {
                         lds_frag_tr(fkt[E], sm.k, SM::LQ, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * E, pp);
-                        accZ[E] = mma(fkt[E], ones, accZ[E]);
+                        accZ[E] = mma(fkt[E], fw, accZ[E]);
+                        if (weighted && sizeof(TC) == 2) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
                     }
 #pragma unroll
                     for (int cs = 0; cs < CBW; ++cs) {

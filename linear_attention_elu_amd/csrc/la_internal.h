@@ -29,8 +29,7 @@ struct DecodeDesc {
 };
 
 struct BwdDesc {
-    const void *q, *k, *v, *o;
-    const float *den;
+    const void *q, *k, *v;
     const void *dO;
     void *dq, *dk, *dv;
     int B, H, N, DK, DV, C;
@@ -47,17 +46,18 @@ struct BwdDesc {
 constexpr long kMaxTargetWg = 2048;
 int plan_segments(long BH, int N, int C, long target_wg, int *L);
 
-// Workgroups of `kernel` (256 threads) the current device keeps resident at
+// Workgroups of `kernel` (`threads` per workgroup) the current device keeps resident at
 // once: occupancy per CU times the CU count, at most kMaxTargetWg.  Cached per
-// device and per `slot` (0..95), which must identify the kernel.
-long resident_workgroups(const void *kernel, int slot);
+// device and per `slot` (0..159), which must identify the kernel.
+long resident_workgroups(const void *kernel, int slot, int threads = 256);
 
 // Floats per stored state: S (DK x DV) followed by z (DK).
 inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 
 // Per-(bh, element) pass over the P segment states stored at ws[bh][P][DK*DV + DK]:
 // mode 0 replaces them by their exclusive prefix (S0, z0 folded in when given),
-// mode 1 writes their total into segment slot 0.  Fixed summation order.
+// mode 1 writes their total into segment slot 0, mode 2 replaces them by their
+// exclusive suffix.  Fixed summation order.
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
                            int mode, hipStream_t stream);
 

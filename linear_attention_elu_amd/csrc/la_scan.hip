@@ -11,8 +11,9 @@
 
 namespace la {
 
-// Prefix over segments, per (bh, element): exclusive prefix (mode 0, the
-// initial state folded in) or total into slot 0 (mode 1).  Fixed order.
+// Pass over segments, per (bh, element): exclusive prefix (mode 0, the
+// initial state folded in), total into slot 0 (mode 1) or exclusive suffix
+// (mode 2).  Fixed order.
 static __global__ void __launch_bounds__(256)
 la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode) {
     const int SS = DK * DV + DK;
@@ -32,10 +33,17 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
             base[(long)s * SS] = run;
             run += a;
         }
-    } else {
+    } else if (mode == 1) {
         float run = 0.f;
         for (int s = 0; s < P; ++s) run += base[(long)s * SS];
         base[0] = run;
+    } else {
+        float run = 0.f;  // exclusive suffix: the sum over the later segments
+        for (int s = P - 1; s >= 0; --s) {
+            const float a = base[(long)s * SS];
+            base[(long)s * SS] = run;
+            run += a;
+        }
     }
 }
 

@@ -108,19 +108,27 @@ def test_fwd_noncausal_rejects(lib):
 
 def test_bwd_causal_rejects(lib):
     f = lib.la_bwd_causal
-    args = [P] * 9 + [1, 1, 64, 64, 64, 64, 1, P, 1 << 24, None]
+    need = la.la_bwd_causal_workspace_bytes(1, 1, 64, 64, 64, 64)
+    assert need > 0
+    args = [P] * 7 + [1, 1, 64, 64, 64, 64, 1, P, need, None]
     bad = list(args)
-    bad[4] = None  # den
+    bad[3] = None  # dO
     assert f(*bad) == 1
     bad = list(args)
-    bad[13] = 96  # d_v
+    bad[11] = 96  # d_v
     assert f(*bad) == 3
     bad = list(args)
-    bad[15] = 3  # dtype
+    bad[13] = 3  # dtype
     assert f(*bad) == 4
     bad = list(args)
-    bad[8] = MIS  # dv
+    bad[6] = MIS  # dv
     assert f(*bad) == 7
+    bad = list(args)
+    bad[14] = None  # the workspace is always required
+    assert f(*bad) == 5
+    bad = list(args)
+    bad[15] = need - 1
+    assert f(*bad) == 5
 
 
 def test_decode_rejects(lib):

@@ -1,0 +1,92 @@
+"""Parity of the cumulative-sum backward with the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_elu_amd as la
+import oracle
+from gpu_util import announce, assert_close, device_inputs, max_abs, need_gpu, row_rel_l2, to64
+
+pytestmark = pytest.mark.gpu
+
+BWD_CASES = [
+    (2, 1, 64, 16, 32, 16),
+    (2, 1, 50, 16, 32, 16),    # ragged last chunk
+    (1, 1, 1, 64, 64, 64),     # a single token
+    (1, 2, 200, 64, 64, 64),
+    (1, 3, 333, 64, 128, 32),
+    (2, 1, 129, 128, 32, 16),
+    (1, 1, 700, 128, 128, 64),
+    (1, 2, 777, 32, 64, 64),
+    (3, 1, 96, 16, 16, 32),
+]
+
+
+def run_bwd(x, C):
+    return la.la_bwd_causal(x["q"], x["k"], x["v"], x["dO"], C=C)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B{}_H{}_N{}_dk{}_dv{}_C{}".format(*c))
+def test_backward_matches_oracle(case, dtype):
+    dev = need_gpu()
+    B, H, N, dk, dv, C = case
+    announce(f"bwd {dtype} {case}")
+    x, x64 = device_inputs(B, H, N, dk, dv, dtype, seed=sum(case) + 1, with_grad=True)
+    dq, dkk, dvv = run_bwd(x, C)
+    torch.cuda.synchronize(dev)
+    rq, rk, rv = oracle.bwd_causal(x64["q"], x64["k"], x64["v"], x64["dO"])
+    # unit-scale inputs: gradient rows are O(1e-2 .. 1); 1e-3 is the absolute
+    # floor for blocks whose exact gradient is zero throughout (a single token)
+    assert_close(to64(dq), rq, dtype, "dq", abs_floor=1e-3)
+    assert_close(to64(dkk), rk, dtype, "dk", abs_floor=1e-3)
+    assert_close(to64(dvv), rv, dtype, "dv", abs_floor=1e-3)
+
+
+def test_backward_workload_sampled():
+    """Causal forward + backward at B=8, H=16, N=8192, d=128, C=64, bf16, seed 0,
+    as the benchmark runs it; the oracle checks every row of three sampled
+    (batch, head) pairs."""
+    dev = need_gpu()
+    B, H, N, d = 8, 16, 8192, 128
+    announce("bwd workload")
+    x, _ = device_inputs(B, H, N, d, d, "bf16", seed=0, with_grad=True, exact=False)
+    dq, dkk, dvv = run_bwd(x, 64)
+    torch.cuda.synchronize(dev)
+    for (b, h) in [(0, 0), (4, 9), (7, 15)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.bwd_causal(*(to64(x[n][sl]) for n in ("q", "k", "v", "dO")))
+        for name, got, ref in (("dq", dq, rq), ("dk", dkk, rk), ("dv", dvv, rv)):
+            err = row_rel_l2(to64(got[sl]), ref)
+            print(f"(b={b}, h={h}) {name}: row-wise relative L2 {err:.3e}")
+            assert err <= 2e-2, (b, h, name, err)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_invariants(dtype):
+    """Value gradients sum to the upstream gradients (each output's weights sum
+    to one); with all value rows equal, dq and dk vanish."""
+    dev = need_gpu()
+    x, _ = device_inputs(2, 2, 300, 64, 32, dtype, seed=21, with_grad=True, exact=False)
+    _, _, dvv = run_bwd(x, 64)
+    torch.cuda.synchronize(dev)
+    lhs = to64(dvv).sum(axis=2)
+    rhs = to64(x["dO"]).sum(axis=2)
+    tol = 1e-3 if dtype == "f32" else 5e-2
+    assert np.abs(lhs - rhs).max() <= tol * np.abs(rhs).max()
+    c = torch.randn(32, generator=torch.Generator().manual_seed(3)).to(x["v"].dtype).to(dev)
+    x["v"] = c.expand_as(x["v"]).contiguous()
+    dq, dkk, _ = run_bwd(x, 64)
+    torch.cuda.synchronize(dev)
+    scale = np.abs(to64(x["dO"])).max()
+    assert max_abs(to64(dq), 0 * to64(dq)) <= (1e-4 if dtype == "f32" else 2e-2) * scale
+    assert max_abs(to64(dkk), 0 * to64(dkk)) <= (1e-4 if dtype == "f32" else 2e-2) * scale
+
+
+def test_backward_is_deterministic():
+    dev = need_gpu()
+    x, _ = device_inputs(2, 4, 2048, 64, 64, "bf16", seed=22, with_grad=True, exact=False)
+    r1 = run_bwd(x, 64)
+    r2 = run_bwd(x, 64)
+    torch.cuda.synchronize(dev)
+    assert all(torch.equal(a, b) for a, b in zip(r1, r2))
