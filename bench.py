@@ -56,6 +56,29 @@ def parse():
     return ap.parse_args()
 
 
+def profiled_traffic(summary: str):
+    """HBM bytes per call recorded in profiles/<summary> from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes, or None when the kernel sources changed since they were taken."""
+    import glob
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_call", "kernel_source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_elu_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_call" not in fields:
+        return None
+    return int(float(fields["traffic_bytes_per_call"]))
+
+
 def time_calls(fn, steps, warmup, stream):
     import torch
 
@@ -288,7 +311,9 @@ def main():
         "config": {"workload": "causal_fwd_bf16_B8_H8_N65536_d64_C64", "B": 8, "H": 8, "N": 65536,
                    "d_k": 64, "d_v": 64, "C": 64, "out": "bf16"},
         "roofline": {"bound": "hbm", "achieved": round(f["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(f["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(f["gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("causal_fwd_bf16_B8_H8_N65536_d64_C64.md"),
+                     "traffic_unit": "HBM bytes per la_fwd_causal call (rocprofv3 counters, calibrated)",
                      "kernel": "la_fwd_causal (segment aggregate + segment scan + chunk loop)",
                      "bytes_per_launch": f["bytes"]},
         "mfma": {"achieved": round(f["tflops"], 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -300,6 +325,7 @@ def main():
     if not args.no_decode:
         log("decode: 3072 steps, graph replay")
         res["decode"] = bench_decode(dev)
+        res["decode"]["traffic"] = profiled_traffic("decode_fp32_B256_H8_d32.md")
         log(f"decode {res['decode']['us_per_step']} us/step")
     if not args.no_extra:
         log("extra: length sweep, non-causal, fwd+bwd")
