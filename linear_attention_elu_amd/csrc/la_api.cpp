@@ -22,13 +22,11 @@ int plan_segments(long BH, int N, int C, long target_wg, int *L) {
     return (int)P;
 }
 
-long resident_workgroups(const void *kernel, int slot, int threads) {
-    constexpr int kDevices = 64, kSlots = 160;
-    static std::atomic<long> cache[kDevices][kSlots];
+long resident_workgroups(const void *kernel, OccCache &cache, int threads) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices || slot < 0 || slot >= kSlots) dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
     if (dev >= 0) {
-        const long c = cache[dev][slot].load(std::memory_order_relaxed);
+        const long c = cache.n[dev].load(std::memory_order_relaxed);
         if (c > 0) return c;
     }
     int per_cu = 0, cus = 0;
@@ -38,7 +36,7 @@ long resident_workgroups(const void *kernel, int slot, int threads) {
         cus = 256;
     long n = (long)per_cu * cus;
     if (n > kMaxTargetWg) n = kMaxTargetWg;
-    if (dev >= 0) cache[dev][slot].store(n, std::memory_order_relaxed);
+    if (dev >= 0) cache.n[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

@@ -7,7 +7,7 @@
 #pragma once
 
 #include "la_bwd_impl.hpp"
-#include "la_fwd_impl.hpp"
+#include "la_fwd_launch.hpp"
 #include "la_internal.h"
 
 namespace la {
@@ -42,14 +42,20 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     float *suf = reinterpret_cast<float *>(ws + lay.suf);
     hipError_t err;
 
-    const int kslot = ((DK == 16 ? 0 : DK == 32 ? 1 : DK == 64 ? 2 : 3) * 4 +
-                       (DV == 16 ? 0 : DV == 32 ? 1 : DV == 64 ? 2 : 3)) * 2 + (sizeof(TI) == 2);
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG>;
+    // The aggregate passes reuse the forward's chunk kernel at the caller's chunk size.
+    void (*agg_kernel)(const FwdParams) = nullptr;
+    long target_agg = 0;
+    switch (fwd_chunk<DK, DV, TI>(d.C)) {
+        case 16: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16>(); break;
+        case 32: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32>(); break;
+        case 64: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64>(); break;
+        default: return hipErrorInvalidValue;
+    }
     auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI>;
     auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI>;
-    const long target_agg = resident_workgroups(reinterpret_cast<const void *>(agg_kernel), kslot * 3 + MODE_AGG);
-    const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), 96 + kslot * 2, kBwdThreads);
-    const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), 96 + kslot * 2 + 1, kBwdThreads);
+    static OccCache occ_dq, occ_kv;
+    const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), occ_dq, kBwdThreads);
+    const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
     auto split = [&](long target, int *mult) {
@@ -63,7 +69,6 @@ hipError_t run_bwd_t(const BwdDesc &d) {
 
     FwdParams a{};
     a.N = d.N;
-    a.C = d.C;
     a.L = Lf;
     a.state_P = Pf;
     a.state_mult = 1;

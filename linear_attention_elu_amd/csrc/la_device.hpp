@@ -33,7 +33,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 
 // phi(x) = elu(x) + 1 (slope 1): x + 1 above zero, exp(x) at or below zero.
-__device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+// Evaluated as max(x + 1, exp(-|x|)) without a compare: at or below zero
+// exp(x) >= 1 + x (exp is convex), above zero exp(-x) < 1 < x + 1.  Where the
+// two candidates are within an ulp of each other (|x| tiny) both are exp(x)
+// to fp32 rounding.  NaN propagates; exp(-inf) = 0 gives phi(-inf) = 0.
+__device__ __forceinline__ float phi(float x) {
+    return fmaxf(x + 1.0f, __builtin_amdgcn_exp2f(-fabsf(x) * 1.44269504088896341f));
+}
 
 // phi'(x): 1 above zero, exp(x) at or below zero.
 __device__ __forceinline__ float dphi(float x) { return x > 0.0f ? 1.0f : __expf(x); }
@@ -52,6 +58,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 
 __device__ __forceinline__ float round_bf16(float x) {
     return static_cast<float>(static_cast<__bf16>(x));
+}
+
+// Four floats to four bf16 (round to nearest even), packed in 8 bytes.
+__device__ __forceinline__ uint2 pack_bf16x4(const f32x4 &x) {
+    const bf16x4 b = __builtin_convertvector(x, bf16x4);
+    return __builtin_bit_cast(uint2, b);
 }
 
 // ---------------------------------------------------------------------------

@@ -10,18 +10,24 @@
 
 namespace la {
 
-template <int DK, int DV, typename TI>
-hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
+// Resident workgroups of one instantiation of the chunk kernel (cached).
+template <int DK, int DV, typename TI, int MODE, int CT>
+long chunk_resident() {
+    static OccCache cache;
+    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT>), cache);
+}
+
+template <int DK, int DV, typename TI, int CT>
+hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    const int kslot = ((DK == 16 ? 0 : DK == 32 ? 1 : DK == 64 ? 2 : 3) * 4 +
-                       (DV == 16 ? 0 : DV == 32 ? 1 : DV == 64 ? 2 : 3)) * 2 + (sizeof(TI) == 2);
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG>;
-    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL> : &la_chunk_kernel<DK, DV, TI, MODE_APPLY>;
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT>;
+    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT>
+                              : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
-    const long target_agg = resident_workgroups(reinterpret_cast<const void *>(agg_kernel), kslot * 3 + MODE_AGG);
-    const long target_main = resident_workgroups(reinterpret_cast<const void *>(main_kernel),
-                                                 kslot * 3 + (causal ? MODE_CAUSAL : MODE_APPLY));
+    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT>();
+    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT>()
+                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT>();
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
     const long want_main = (target_main + BH - 1) / BH;
@@ -35,7 +41,6 @@ hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     p.o = d.o;
     p.den = d.den;
     p.N = d.N;
-    p.C = d.C;
     p.out_bf16 = d.out_bf16;
     p.state_P = Pf;
     hipError_t err;
@@ -78,6 +83,24 @@ hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     p.L = La;
     main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), kThreads, 0, d.stream>>>(p);
     return hipGetLastError();
+}
+
+// Chunk size the kernels run at for a requested C: fp32 operands with a
+// 128-wide head dimension tile 64-token chunks as two of 32 (registers); the
+// result does not depend on the chunk size, and segment lengths stay
+// multiples of the requested C.
+template <int DK, int DV, typename TI> constexpr int fwd_chunk(int C) {
+    return (sizeof(TI) == 4 && (DK == 128 || DV == 128) && C > 32) ? 32 : C;
+}
+
+template <int DK, int DV, typename TI>
+hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
+    switch (fwd_chunk<DK, DV, TI>(d.C)) {
+        case 16: return run_fwd_ct<DK, DV, TI, 16>(d, causal);
+        case 32: return run_fwd_ct<DK, DV, TI, 32>(d, causal);
+        case 64: return run_fwd_ct<DK, DV, TI, 64>(d, causal);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int DK>

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+
 namespace la {
 
 struct FwdDesc {
@@ -48,8 +50,13 @@ int plan_segments(long BH, int N, int C, long target_wg, int *L);
 
 // Workgroups of `kernel` (`threads` per workgroup) the current device keeps resident at
 // once: occupancy per CU times the CU count, at most kMaxTargetWg.  Cached per
-// device and per `slot` (0..159), which must identify the kernel.
-long resident_workgroups(const void *kernel, int slot, int threads = 256);
+// device in `cache`, which belongs to that one kernel (a function-local static
+// of the launcher that names the kernel).
+constexpr int kMaxDevices = 64;
+struct OccCache {
+    std::atomic<long> n[kMaxDevices];
+};
+long resident_workgroups(const void *kernel, OccCache &cache, int threads = 256);
 
 // Floats per stored state: S (DK x DV) followed by z (DK).
 inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
