@@ -42,13 +42,27 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     float *suf = reinterpret_cast<float *>(ws + lay.suf);
     hipError_t err;
 
-    // The aggregate passes reuse the forward's chunk kernel at the caller's chunk size.
+    // The aggregate passes reuse the forward's chunk kernel at the caller's
+    // chunk size: plain for the prefix sums, weighted for the suffix sums.
     void (*agg_kernel)(const FwdParams) = nullptr;
+    void (*aggw_kernel)(const FwdParams) = nullptr;
     long target_agg = 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
-        case 16: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16>(); break;
-        case 32: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32>(); break;
-        case 64: agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64>; target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64>(); break;
+        case 16:
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 16, false>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16>();
+            break;
+        case 32:
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 32, false>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32>();
+            break;
+        case 64:
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 64, false>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64>();
+            break;
         default: return hipErrorInvalidValue;
     }
     auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI>;
@@ -76,7 +90,7 @@ hipError_t run_bwd_t(const BwdDesc &d) {
         a.k = d.k;
         a.v = d.v;
         a.seg_out = pre;
-        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(a);
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
     }
@@ -107,7 +121,7 @@ hipError_t run_bwd_t(const BwdDesc &d) {
         a.kscale = inv_den;
         a.zw = eps;
         a.seg_out = suf;
-        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(a);
+        aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, d.stream)) != hipSuccess) return err;
     }

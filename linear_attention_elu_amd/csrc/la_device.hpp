@@ -146,6 +146,44 @@ __device__ __forceinline__ void lds_frag_split(Frag<float> &f, const float *row0
     }
 }
 
+// A copy of an LDS address the compiler cannot relate to other addresses
+// (a register move it does not see through).  Reads from bases made this way
+// are never merged with each other: the compiler would otherwise pair the
+// two 8-byte halves of split fragments (32 or 64 bytes apart) into one
+// ds_read2_b64, which on gfx950 serves a wave with several times the bank
+// conflicts of two ds_read_b64 (LDS conflict counters: 16 against 4 cycles
+// per fragment at a 144-byte row stride).
+template <typename T> using lds_cptr = const T __attribute__((address_space(3))) *;
+
+template <typename TC> __device__ __forceinline__ lds_cptr<TC> lds_opaque(const TC *p) {
+    uint32_t a = (uint32_t)(uintptr_t)(lds_cptr<TC>)p;  // generic -> LDS address
+    asm("v_mov_b32 %0, %1" : "=v"(a) : "v"(a));
+    return (lds_cptr<TC>)(uintptr_t)a;
+}
+
+// Split-assignment fragment from two per-lane LDS bases (the lane's slots
+// 0..3 at lo[off..], slots 4..7 at hi[off..]).
+template <typename TC>
+__device__ __forceinline__ void lds_frag_split_at(Frag<TC> &f, lds_cptr<TC> lo, lds_cptr<TC> hi, int off) {
+    if constexpr (sizeof(TC) == 2) {
+        const bf16x4 a = *reinterpret_cast<lds_cptr<bf16x4>>(lo + off);
+        const bf16x4 b = *reinterpret_cast<lds_cptr<bf16x4>>(hi + off);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f.v[t] = a[t];
+            f.v[t + 4] = b[t];
+        }
+    } else {
+        const f32x4 a = *reinterpret_cast<lds_cptr<f32x4>>(lo + off);
+        const f32x4 b = *reinterpret_cast<lds_cptr<f32x4>>(hi + off);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            f.v[t] = a[t];
+            f.v[t + 4] = b[t];
+        }
+    }
+}
+
 // Transposed reads of a row-major tile (LDS), for operands whose K index is
 // the tile's row index.  The result slots t = 0..3 of the lane at position p
 // are tile[row0 + t][col0 + p] and slots 4..7 are tile[row1 + t][col0 + p];

@@ -4,7 +4,9 @@
 //   MODE_AGG    -- sum phi(K)^T V and sum phi(K) over the segment (no output);
 //   MODE_CAUSAL -- the chunk loop of the causal form, starting from the state
 //                  carried into the segment;
-//   MODE_APPLY  -- the non-causal read-out phi(Q) S / phi(Q) z with a fixed state.
+//   MODE_APPLY  -- the non-causal read-out phi(Q) S / phi(Q) z with a fixed state;
+//   MODE_AGGW   -- MODE_AGG with a per-token factor on each phi(k) row and
+//                  per-token weights in the z sum (the backward's suffix sums).
 // Chunked causal form (itwiki "선형 어텐션", table "Comparison of forms", chunked
 // row, and section "Implementation"): inside a chunk of C tokens the causal
 // scores are a masked matrix product, between chunks the state
@@ -14,30 +16,34 @@
 // (the prefix sum is a scan and can be taken in parallel: blog digest
 // "Theoretical significance / prefix-sum parallelism").
 //
-// Data path of one chunk: the workgroup loads q, k, v rows with 16-byte
-// global loads into registers ahead of use, applies phi to q and k while
-// writing the rows to LDS (row-major, 16-byte writes), and every matrix
-// operand is then read from those row-major tiles -- with plain reads where
-// the contraction runs over features and with the gfx950 transpose read
-// (ds_read_b64_tr_b16) where it runs over tokens.  When two sets of tiles fit
-// in LDS they are double buffered: one step writes chunk c + 1 into one
-// buffer while it computes chunk c from the other, with a single barrier per
-// chunk, so the vector work of staging overlaps the matrix and LDS work.
-// The chunks of a segment whose rows are all valid run in a loop of their
-// own (unrolled by two, so buffer offsets are immediates), addressed from a
-// uniform per-chunk base plus fixed per-lane offsets, without row masks; the
-// last one or two chunks run a general loop with clamped loads and masks.
-// The chunk size is a template parameter, so every tile loop is unrolled.
+// For bf16 with d_k, d_v <= 64 a workgroup is eight waves with two roles, one
+// wave of each role on every SIMD, so that the vector work of one overlaps
+// the matrix work of the other:
+//   * staging waves (4..7) load q, k, v rows with 16-byte global loads two
+//     chunks ahead into registers (two register sets, alternating), apply phi
+//     to q and k and write the rows to LDS (row-major, 16-byte writes);
+//   * compute waves (0..3) read every matrix operand from those row-major
+//     tiles -- with plain reads where the contraction runs over features and
+//     with the gfx950 transpose read (ds_read_b64_tr_b16) where it runs over
+//     tokens -- run the MFMA work and store the outputs.
+// The tiles are double buffered: while the compute waves work on chunk c the
+// staging waves fill chunk c + 1, with a single barrier per chunk.  Wider
+// heads and fp32, whose compute waves need more registers than two waves per
+// SIMD leave, use four waves that do both jobs in turn (stage chunk c + 1,
+// compute chunk c) with one register set.  Chunks
+// whose rows are all valid run an unrolled loop (buffer and register-set
+// indices are constants) with fixed per-lane offsets from a uniform base and
+// no row masks; the last chunks run a general loop with clamped loads.
 //
-// Work split inside a workgroup of four waves: wave w owns value-column
-// blocks cb = w, w + 4, ... (16 columns each).  Its slice S[:, cb] of the
-// state lives in accumulator registers for the whole segment and is fed back
-// to the matrix cores as an operand through the split K assignment (see
-// la_device.hpp), so the carry never leaves the registers; the normaliser z
-// is carried the same way, as phi(K)^T times an all-ones operand.  Each wave
-// computes the transposed score tiles A^T = phi(K) phi(Q)^T itself and the
-// transposed output O^T(cb) = V^T(cb) A^T + S(cb)^T phi(Q)^T, which puts each
-// query's normaliser in the lanes that store that query's outputs.
+// Compute split: compute wave w owns value-column blocks cb = w, w + 4, ...
+// (16 columns each).  Its slice S[:, cb] of the state lives in accumulator
+// registers for the whole segment and is fed back to the matrix cores as an
+// operand through the split K assignment (see la_device.hpp), so the carry
+// never leaves the registers; the normaliser z is carried the same way, as
+// phi(K)^T times an all-ones operand.  Each compute wave computes the
+// transposed score tiles A^T = phi(K) phi(Q)^T itself and the transposed
+// output O^T(cb) = V^T(cb) A^T + S(cb)^T phi(Q)^T, which puts each query's
+// normaliser in the lanes that store that query's outputs.
 #pragma once
 
 #include <type_traits>
@@ -46,9 +52,19 @@
 
 namespace la {
 
-enum { MODE_AGG = 0, MODE_CAUSAL = 1, MODE_APPLY = 2 };
+enum { MODE_AGG = 0, MODE_CAUSAL = 1, MODE_APPLY = 2, MODE_AGGW = 3 };
 
-constexpr int kThreads = 256;  // four waves
+constexpr int kRoleThreads = 256;  // four waves per role
+
+// Separate staging and compute waves (eight per workgroup) where the compute
+// waves fit in the registers two waves per SIMD leave; otherwise four waves
+// take both roles.
+template <int DK, int DV, typename TI> constexpr bool fwd_split() {
+    return sizeof(TI) == 2 && DK <= 64 && DV <= 64;
+}
+template <int DK, int DV, typename TI> constexpr int fwd_threads() {
+    return fwd_split<DK, DV, TI>() ? 2 * kRoleThreads : kRoleThreads;
+}
 
 struct FwdParams {
     const void *q;
@@ -59,16 +75,15 @@ struct FwdParams {
     const float *seg_state; // per (bh, segment) entering state [DK*DV + DK], or null
     const float *S0;        // per-bh initial state, used only when seg_state is null
     const float *z0;
-    float *seg_out;         // MODE_AGG: per (bh, segment) aggregates
-    const float *zw;        // MODE_AGG: per-token weights [BH][N] for z (null: all ones)
-    const float *kscale;    // MODE_AGG: per-token factors [BH][N] applied to phi(k) rows (null: none)
+    float *seg_out;         // MODE_AGG(W): per (bh, segment) aggregates
+    const float *zw;        // MODE_AGGW: per-token weights [BH][N] for z
+    const float *kscale;    // MODE_AGGW: per-token factors [BH][N] applied to phi(k) rows
     float *S_fin;           // final state of the last segment (nullable)
     float *z_fin;
     int N;
     int L;                  // tokens per segment of this launch (a multiple of the chunk size)
     int state_P;            // segments per (bh) in the state array
     int state_mult;         // segment s of this launch starts at state slot s * state_mult
-    int out_bf16;
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -76,61 +91,76 @@ struct FwdParams {
 // per-token z weights.
 template <int DK, int DV, typename TC, int CT, int MODE> struct FwdTiles {
     static constexpr int DKP = DK < 32 ? 32 : DK;        // feature dim padded to a K step
-    static constexpr int PAD = 16 / sizeof(TC);          // 16-byte row padding
+    // Row padding, in elements, against LDS bank conflicts (64 banks of 4
+    // bytes; a 64-lane 8-byte read is served 32 lanes per cycle): 16 bytes
+    // suit the row-wise operand reads of the q and k tiles; the v tile is
+    // read only transposed, four rows per lane group with the lane groups
+    // four rows apart, which 32 bytes of bf16 padding make conflict-free.
+    static constexpr int PAD = 16 / sizeof(TC);
+    static constexpr int PADV = sizeof(TC) == 2 ? 16 : 4;
     static constexpr int LQ = DKP + PAD;                  // row length of q, k tiles
-    static constexpr int LV = DV + PAD;                   // row length of the v tile
+    static constexpr int LV = DV + PADV;                  // row length of the v tile
     static constexpr int ROWS = CT < 32 ? 32 : CT;        // chunk rows padded to a token K step
-    static constexpr int QB = MODE != MODE_AGG ? ROWS * LQ * (int)sizeof(TC) : 0;
+    static constexpr int QB = MODE == MODE_CAUSAL || MODE == MODE_APPLY ? ROWS * LQ * (int)sizeof(TC) : 0;
     static constexpr int KB = MODE != MODE_APPLY ? ROWS * LQ * (int)sizeof(TC) : 0;
     static constexpr int VB = MODE != MODE_APPLY ? ROWS * LV * (int)sizeof(TC) : 0;
-    static constexpr int WB = MODE == MODE_AGG ? ROWS * 4 : 0;
+    static constexpr int WB = MODE == MODE_AGGW ? ROWS * 4 : 0;
     static constexpr int OFF_Q = 0, OFF_K = QB, OFF_V = QB + KB, OFF_W = QB + KB + VB;
     static constexpr int BUF = QB + KB + VB + WB;          // bytes per buffer (multiple of 16)
-    static constexpr int NBUF = 2 * BUF <= 64 * 1024 ? 2 : 1;  // double buffer when it stays small
-    static constexpr int LDS_WG = (160 * 1024) / (NBUF * BUF);  // workgroups per CU that LDS allows
+    // Double buffering where it leaves room: a split workgroup has its CU's
+    // LDS to itself; four-wave workgroups keep the buffers small.
+    static constexpr int NBUF = 2 * BUF <= (fwd_split<DK, DV, TC>() ? 150 : 64) * 1024 ? 2 : 1;
 };
 
 // Waves per SIMD the compiler must leave room for (registers are split among
-// them) in the d <= 64 bf16 kernels: as many workgroups as LDS admits, capped
-// where the causal chunk loop needs more registers than that would leave
-// (two waves for 64-token chunks, three for smaller ones); one otherwise.
+// them).  A split workgroup puts two waves on every SIMD; its causal chunk
+// loop needs the registers of one workgroup per CU, its aggregate and
+// read-out passes fit two.  Four-wave workgroups get all registers.
 template <int DK, int DV, typename TI, int CT, int MODE> constexpr int fwd_waves_per_eu() {
-    constexpr int lds = FwdTiles<DK, DV, TI, CT, MODE>::LDS_WG;
-    constexpr int cap = MODE == MODE_CAUSAL ? (CT == 64 ? 2 : 3) : 4;
-    return (sizeof(TI) == 2 && DK <= 64 && DV <= 64) ? (lds < 1 ? 1 : lds > cap ? cap : lds) : 1;
+    return fwd_split<DK, DV, TI>() ? (MODE != MODE_CAUSAL ? 4 : 2) : 1;
 }
 
 #define LA_INLINE __attribute__((always_inline))
 
-template <int DK, int DV, typename TI, int MODE, int CT>
-__global__ void __launch_bounds__(kThreads)
+// OBF: the output o is bf16 (else fp32).
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF>
+__global__ void __launch_bounds__((fwd_threads<DK, DV, TI>()))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE>())))
 la_chunk_kernel(const FwdParams p) {
     using TC = TI;  // matrix operands keep the input precision
     using T = FwdTiles<DK, DV, TC, CT, MODE>;
+    constexpr bool SPLIT = fwd_split<DK, DV, TI>();
+    constexpr int kThreads = fwd_threads<DK, DV, TI>();
     constexpr int NBUF = T::NBUF;
     constexpr int VEC = Store<TI>::VEC;
     constexpr int NE = DK / 16;            // feature tiles
     constexpr int NSE = (DK + 31) / 32;    // feature K steps
     constexpr int CBT = DV / 16;           // value-column blocks in total
-    constexpr int CBW = (CBT + 3) / 4;     // per wave (at most)
+    constexpr int CBW = (CBT + 3) / 4;     // per compute wave (at most)
     constexpr int NB = CT / 16;            // query/key row blocks per chunk
     constexpr int NP = (NB + 1) / 2;       // pairs of row blocks (token K steps)
     constexpr int VQ = DK / VEC;           // 16-byte vectors per q/k row
     constexpr int VV = DV / VEC;           // per v row
-    constexpr int NLQ = (CT * VQ + kThreads - 1) / kThreads;
-    constexpr int NLV = (CT * VV + kThreads - 1) / kThreads;
-    constexpr int RSQ = kThreads / VQ;     // rows between a thread's q/k vectors
-    constexpr int RSV = kThreads / VV;
-    constexpr bool NEED_Q = MODE != MODE_AGG;
+    constexpr int NLQ = (CT * VQ + kRoleThreads - 1) / kRoleThreads;  // vectors per staging thread
+    constexpr int NLV = (CT * VV + kRoleThreads - 1) / kRoleThreads;
+    constexpr int RSQ = kRoleThreads / VQ; // rows between a staging thread's q/k vectors
+    constexpr int RSV = kRoleThreads / VV;
+    constexpr bool NEED_Q = MODE == MODE_CAUSAL || MODE == MODE_APPLY;
+    constexpr bool AGGM = MODE == MODE_AGG || MODE == MODE_AGGW;  // aggregate only
+    constexpr bool WEIGHTED = MODE == MODE_AGGW;
     constexpr bool NEED_K = MODE != MODE_APPLY;
-    constexpr int NKS = MODE == MODE_AGG ? NLQ : 1;  // per-vector phi(k) factors
+    constexpr int NKS = WEIGHTED ? NLQ : 1;  // per-vector phi(k) factors
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    using S0t = std::integral_constant<int, 0>;
+    using S1t = std::integral_constant<int, 1>;
 
     __shared__ __attribute__((aligned(16))) char smem[NBUF * T::BUF];
 
     const int tid = threadIdx.x;
+    const bool stager = SPLIT && tid >= kRoleThreads;  // uniform per wave
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = (tid >> 6) & 3;          // index inside the role
     const int g = lane >> 4;
     const int pp = lane & 15;
     const long bh = blockIdx.x;
@@ -140,27 +170,203 @@ la_chunk_kernel(const FwdParams p) {
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + CT - 1) / CT;
     const int nfull = (row_end - row_begin) / CT;   // chunks with all CT rows valid
-    const bool has_cols = wave < CBT;               // waves without value columns only stage data
-    const bool weighted = MODE == MODE_AGG && p.zw != nullptr;
-    const bool kscaled = MODE == MODE_AGG && p.kscale != nullptr;
-
-    // Segment bases (uniform); chunk c starts CT rows further per chunk.
     const long seg_row0 = bh * N + row_begin;
-    const char *qs = static_cast<const char *>(p.q) + seg_row0 * DK * (long)sizeof(TI);
-    const char *ks = static_cast<const char *>(p.k) + seg_row0 * DK * (long)sizeof(TI);
-    const char *vs = static_cast<const char *>(p.v) + seg_row0 * DV * (long)sizeof(TI);
-
-    // Per-lane offsets of this thread's first staged vector (row, column).
-    const int rq0 = tid / VQ, cq0 = (tid % VQ) * VEC;
-    const int rv0 = tid / VV, cv0 = (tid % VV) * VEC;
-    const unsigned gq0 = (unsigned)(rq0 * DK + cq0) * sizeof(TI);
-    const unsigned gv0 = (unsigned)(rv0 * DV + cv0) * sizeof(TI);
-    const int lq0 = (rq0 * T::LQ + cq0) * (int)sizeof(TC);
-    const int lv0 = (rv0 * T::LV + cv0) * (int)sizeof(TC);
+    auto rows_of = [&](int c) { return min(CT, row_end - row_begin - c * CT); };
+    if (nch <= 0) return;  // no launched segment is empty; uniform for the workgroup
 
     // ---- zero the tile storage once: padding rows and columns stay zero ----
     for (int i = tid; i < NBUF * T::BUF / 16; i += kThreads)
         reinterpret_cast<uint4 *>(smem)[i] = make_uint4(0u, 0u, 0u, 0u);
+
+    // ================= staging (both layouts) =================
+    const int sid = SPLIT ? tid - kRoleThreads : tid;  // staging thread index 0..255
+        constexpr bool weighted = WEIGHTED, kscaled = WEIGHTED;
+        const char *qs = static_cast<const char *>(p.q) + seg_row0 * DK * (long)sizeof(TI);
+        const char *ks = static_cast<const char *>(p.k) + seg_row0 * DK * (long)sizeof(TI);
+        const char *vs = static_cast<const char *>(p.v) + seg_row0 * DV * (long)sizeof(TI);
+        // This thread's first vector (row, column); vector i is RSQ (RSV) rows further.
+        const int rq0 = sid / VQ, cq0 = (sid % VQ) * VEC;
+        const int rv0 = sid / VV, cv0 = (sid % VV) * VEC;
+        const unsigned gq0 = (unsigned)(rq0 * DK + cq0) * sizeof(TI);
+        const unsigned gv0 = (unsigned)(rv0 * DV + cv0) * sizeof(TI);
+        const int lq0 = (rq0 * T::LQ + cq0) * (int)sizeof(TC);
+        const int lv0 = (rv0 * T::LV + cv0) * (int)sizeof(TC);
+        // Vectors past the chunk exist only when CT * VQ is not a multiple of
+        // the role size; they re-read the chunk's last row and are not staged.
+        auto q_on = [&](int i) { return (CT * VQ) % kRoleThreads == 0 || rq0 + i * RSQ < CT; };
+        auto v_on = [&](int i) { return (CT * VV) % kRoleThreads == 0 || rv0 + i * RSV < CT; };
+
+        // Two register sets; chunk j lives in set j & 1.
+        uint4 rq[2][NEED_Q ? NLQ : 1], rk[2][NEED_K ? NLQ : 1], rv[2][NEED_K ? NLV : 1];
+        float rw[2] = {0.f, 0.f};
+        float rks[2][NKS];
+
+        // Load chunk c into set S.  FULL: all rows valid (uniform base, fixed
+        // lane offsets); otherwise row indices are clamped to the segment.
+        auto load = [&](auto set_tag, auto full_tag, int c) LA_INLINE {
+            constexpr int S = decltype(set_tag)::value;
+            constexpr bool FULL = decltype(full_tag)::value;
+            const int r0 = c * CT;
+            const int last = FULL ? r0 + CT - 1 : row_end - row_begin - 1;  // segment-relative
+            if (weighted) rw[S] = (sid < CT && r0 + sid <= last) ? p.zw[seg_row0 + r0 + sid] : 0.f;
+            if (kscaled) {
+#pragma unroll
+                for (int i = 0; i < NKS; ++i) rks[S][i] = p.kscale[seg_row0 + min(r0 + rq0 + i * RSQ, last)];
+            }
+            if constexpr (FULL) {
+                const char *qc = qs + (long)r0 * DK * (long)sizeof(TI);
+                const char *kc = ks + (long)r0 * DK * (long)sizeof(TI);
+                const char *vc = vs + (long)r0 * DV * (long)sizeof(TI);
+                auto offq = [&](int i) {
+                    return (CT * VQ) % kRoleThreads != 0 && i == NLQ - 1
+                               ? (unsigned)((min(rq0 + i * RSQ, CT - 1) * DK + cq0) * sizeof(TI))
+                               : gq0 + (unsigned)(i * RSQ * DK * sizeof(TI));
+                };
+                auto offv = [&](int i) {
+                    return (CT * VV) % kRoleThreads != 0 && i == NLV - 1
+                               ? (unsigned)((min(rv0 + i * RSV, CT - 1) * DV + cv0) * sizeof(TI))
+                               : gv0 + (unsigned)(i * RSV * DV * sizeof(TI));
+                };
+                if (NEED_Q) {
+#pragma unroll
+                    for (int i = 0; i < NLQ; ++i) rq[S][i] = *reinterpret_cast<const uint4 *>(qc + offq(i));
+                }
+                if (NEED_K) {
+#pragma unroll
+                    for (int i = 0; i < NLQ; ++i) rk[S][i] = *reinterpret_cast<const uint4 *>(kc + offq(i));
+#pragma unroll
+                    for (int i = 0; i < NLV; ++i) rv[S][i] = *reinterpret_cast<const uint4 *>(vc + offv(i));
+                }
+            } else {
+                if (NEED_Q) {
+#pragma unroll
+                    for (int i = 0; i < NLQ; ++i) {
+                        const long row = min(r0 + rq0 + i * RSQ, last);
+                        rq[S][i] = *reinterpret_cast<const uint4 *>(qs + (row * DK + cq0) * (long)sizeof(TI));
+                    }
+                }
+                if (NEED_K) {
+#pragma unroll
+                    for (int i = 0; i < NLQ; ++i) {
+                        const long row = min(r0 + rq0 + i * RSQ, last);
+                        rk[S][i] = *reinterpret_cast<const uint4 *>(ks + (row * DK + cq0) * (long)sizeof(TI));
+                    }
+#pragma unroll
+                    for (int i = 0; i < NLV; ++i) {
+                        const long row = min(r0 + rv0 + i * RSV, last);
+                        rv[S][i] = *reinterpret_cast<const uint4 *>(vs + (row * DV + cv0) * (long)sizeof(TI));
+                    }
+                }
+            }
+        };
+        // Any chunk: one code path (clamped rows), so every load sequence
+        // has the same instructions and the waits computed for it stay exact.
+        auto load_any = [&](auto set_tag, int c) LA_INLINE { load(set_tag, Part{}, c); };
+
+        // phi (times a factor) of a 16-byte vector of inputs, as a 16-byte vector of TC.
+        auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
+            float x[VEC];
+            unpack16(u, x, TI());
+            Frag<TC> w;
+#pragma unroll
+            for (int t = 0; t < VEC; ++t) w.set(t, WEIGHTED ? phi(x[t]) * scale : phi(x[t]));
+            if constexpr (sizeof(TC) == 2) {
+                return __builtin_bit_cast(uint4, w.v);
+            } else {
+                return make_uint4(__float_as_uint(w.get(0)), __float_as_uint(w.get(1)), __float_as_uint(w.get(2)),
+                                  __float_as_uint(w.get(3)));
+            }
+        };
+        // Write set S into LDS buffer b.  FULL: all CT rows valid; otherwise
+        // rows at or beyond nrows are written as zeros (they add nothing).
+        auto stage = [&](auto set_tag, auto full_tag, int b, int nrows) LA_INLINE {
+            constexpr int S = decltype(set_tag)::value;
+            constexpr bool FULL = decltype(full_tag)::value;
+            char *buf = smem + b * T::BUF;
+            if (weighted && sid < T::ROWS) reinterpret_cast<float *>(buf + T::OFF_W)[sid] = rw[S];
+            auto keep = [&](int row) { return FULL || row < nrows; };
+            if (NEED_Q) {
+#pragma unroll
+                for (int i = 0; i < NLQ; ++i) {
+                    if (q_on(i)) {
+                        uint4 out = phi16(rq[S][i], 1.0f);
+                        if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
+                        *reinterpret_cast<uint4 *>(buf + T::OFF_Q + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
+                    }
+                }
+            }
+            if (NEED_K) {
+#pragma unroll
+                for (int i = 0; i < NLQ; ++i) {
+                    if (q_on(i)) {
+                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : 1.0f);
+                        if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
+                        *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < NLV; ++i) {
+                    if (v_on(i)) {
+                        uint4 out = rv[S][i];
+                        if (!keep(rv0 + i * RSV)) out = make_uint4(0u, 0u, 0u, 0u);
+                        *reinterpret_cast<uint4 *>(buf + T::OFF_V + lv0 + i * RSV * T::LV * (int)sizeof(TC)) = out;
+                    }
+                }
+            }
+        };
+        // One step of the split layout's general loop at chunk j: stage chunk
+        // j from its register set, then refill that set with chunk j + 2.
+        auto step_split = [&](auto set_tag, int j) LA_INLINE {
+            const int b = NBUF == 2 ? (j & 1) : 0;
+            if (j < nfull) stage(set_tag, Full{}, b, CT);
+            else stage(set_tag, Part{}, b, rows_of(j));
+            if (j + 2 < nch) load_any(set_tag, j + 2);
+        };
+
+    if constexpr (SPLIT) {
+      if (stager) {
+        // ================= staging waves: their whole loop =================
+        // Step j stages chunk j (register set j & 1) into buffer j & 1 and
+        // refills that set with chunk j + 2, then meets the compute waves at
+        // a barrier.  The loop starts at j = -2 with loads only, so every load
+        // of the steady state is issued by the same instructions and the wait
+        // before staging a set covers that set's loads, not the other's.
+        __syncthreads();  // the zero fill is complete before any tile write
+        int j = -2;
+        if constexpr (NBUF == 2) {
+            // (the first trip, j = -2 < nfull - 1, always runs: it loads chunks 0 and 1)
+            for (; j + 1 < nfull; j += 2) {  // chunks j, j + 1 are full
+                if (j >= 0) stage(S0t{}, Full{}, 0, CT);
+                load_any(S0t{}, j + 2);
+                if (j >= 0) __syncthreads();
+                if (j >= 0) stage(S1t{}, Full{}, 1, CT);
+                load_any(S1t{}, j + 3);
+                if (j >= 0) __syncthreads();
+            }
+            for (; j < nch; ++j) {
+                if (j & 1) step_split(S1t{}, j);
+                else step_split(S0t{}, j);
+                __syncthreads();
+            }
+        } else {
+            load_any(S0t{}, 0);
+            load_any(S1t{}, 1);
+            for (j = 0; j < nch; ++j) {
+                if (j > 0) __syncthreads();  // the compute waves are done with the buffer
+                if (j & 1) step_split(S1t{}, j);
+                else step_split(S0t{}, j);
+                __syncthreads();
+            }
+        }
+        return;
+      }
+    }
+
+    // ================= compute (both layouts) =================
+    // wave = tid / 64 < 4: with a multiple of four column blocks every wave
+    // owns CBW of them, and the tests below fold away.
+    auto col_ok = [&](int cs) { return CBT % 4 == 0 || wave + 4 * cs < CBT; };
+    const bool has_cols = col_ok(0);                // waves without value columns only wait
 
     // ---- state entering this segment ----
     const float *Sin = nullptr;
@@ -189,7 +395,7 @@ la_chunk_kernel(const FwdParams p) {
             const int cb = wave + 4 * cs;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                accS[cs][E][r] = (Sin && cb < CBT) ? Sin[(16 * E + 4 * g + r) * DV + 16 * cb + pp] : 0.0f;
+                accS[cs][E][r] = (Sin && col_ok(cs)) ? Sin[(16 * E + 4 * g + r) * DV + 16 * cb + pp] : 0.0f;
         }
     }
 
@@ -208,7 +414,7 @@ la_chunk_kernel(const FwdParams p) {
             acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
         }
     };
-    if (MODE != MODE_AGG) refresh_state_frags();
+    if (!AGGM) refresh_state_frags();
     Frag<TC> ones;
     frag_ones(ones);
     // causal mask on a diagonal score tile: row 4g + r <= column pp
@@ -216,241 +422,217 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) diag_keep[r] = 4 * g + r <= pp;
 
-    // ---- register prefetch of one chunk ----
-    uint4 rq[NEED_Q ? NLQ : 1], rk[NEED_K ? NLQ : 1], rv[NEED_K ? NLV : 1];
-    float rw = 0.f;
-    float rks[NKS];
-    // Full chunk c: every row is valid; uniform base plus fixed lane offsets.
-    auto load_full = [&](int c) LA_INLINE {
-        const long r0 = (long)c * CT;
-        if (weighted) rw = tid < CT ? p.zw[seg_row0 + r0 + tid] : 0.f;
-        if (kscaled) {
-#pragma unroll
-            for (int i = 0; i < NKS; ++i) rks[i] = p.kscale[seg_row0 + r0 + min(rq0 + i * RSQ, CT - 1)];
-        }
-        const char *qc = qs + r0 * DK * (long)sizeof(TI);
-        const char *kc = ks + r0 * DK * (long)sizeof(TI);
-        const char *vc = vs + r0 * DV * (long)sizeof(TI);
-        // A thread's vectors past the chunk (only when CT * VQ is not a
-        // multiple of the block) re-read the chunk's last row.
-        if (NEED_Q) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const unsigned off = (CT * VQ) % kThreads != 0 && i == NLQ - 1
-                                         ? (unsigned)((min(rq0 + i * RSQ, CT - 1) * DK + cq0) * sizeof(TI))
-                                         : gq0 + (unsigned)(i * RSQ * DK * sizeof(TI));
-                rq[i] = *reinterpret_cast<const uint4 *>(qc + off);
-            }
-        }
-        if (NEED_K) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const unsigned off = (CT * VQ) % kThreads != 0 && i == NLQ - 1
-                                         ? (unsigned)((min(rq0 + i * RSQ, CT - 1) * DK + cq0) * sizeof(TI))
-                                         : gq0 + (unsigned)(i * RSQ * DK * sizeof(TI));
-                rk[i] = *reinterpret_cast<const uint4 *>(kc + off);
-            }
-#pragma unroll
-            for (int i = 0; i < NLV; ++i) {
-                const unsigned off = (CT * VV) % kThreads != 0 && i == NLV - 1
-                                         ? (unsigned)((min(rv0 + i * RSV, CT - 1) * DV + cv0) * sizeof(TI))
-                                         : gv0 + (unsigned)(i * RSV * DV * sizeof(TI));
-                rv[i] = *reinterpret_cast<const uint4 *>(vc + off);
-            }
-        }
-    };
-    // Any chunk c: rows clamped to the segment's last row (the duplicates
-    // are replaced by zeros when staged).
-    auto load_any = [&](int c) LA_INLINE {
-        const int r0 = c * CT;
-        const int last = row_end - row_begin - 1;  // segment-relative
-        if (r0 + CT - 1 <= last) {
-            load_full(c);
-            return;
-        }
-        if (weighted) rw = (tid < CT && r0 + tid <= last) ? p.zw[seg_row0 + r0 + tid] : 0.f;
-        if (kscaled) {
-#pragma unroll
-            for (int i = 0; i < NKS; ++i) rks[i] = p.kscale[seg_row0 + min(r0 + rq0 + i * RSQ, last)];
-        }
-        if (NEED_Q) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const long row = min(r0 + rq0 + i * RSQ, last);
-                rq[i] = *reinterpret_cast<const uint4 *>(qs + (row * DK + cq0) * (long)sizeof(TI));
-            }
-        }
-        if (NEED_K) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const long row = min(r0 + rq0 + i * RSQ, last);
-                rk[i] = *reinterpret_cast<const uint4 *>(ks + (row * DK + cq0) * (long)sizeof(TI));
-            }
-#pragma unroll
-            for (int i = 0; i < NLV; ++i) {
-                const long row = min(r0 + rv0 + i * RSV, last);
-                rv[i] = *reinterpret_cast<const uint4 *>(vs + (row * DV + cv0) * (long)sizeof(TI));
-            }
-        }
-    };
-
-    // phi (times a factor) of a 16-byte vector of inputs, as a 16-byte vector of TC.
-    auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
-        float x[VEC];
-        unpack16(u, x, TI());
-        Frag<TC> w;
-#pragma unroll
-        for (int t = 0; t < VEC; ++t) w.set(t, MODE == MODE_AGG ? phi(x[t]) * scale : phi(x[t]));
-        if constexpr (sizeof(TC) == 2) {
-            return __builtin_bit_cast(uint4, w.v);
-        } else {
-            return make_uint4(__float_as_uint(w.get(0)), __float_as_uint(w.get(1)), __float_as_uint(w.get(2)),
-                              __float_as_uint(w.get(3)));
-        }
-    };
-    // Stage the prefetched chunk into LDS buffer b.  FULL: all CT rows valid;
-    // otherwise rows at or beyond nrows are written as zeros (they add nothing).
-    auto stage = [&](auto full_tag, int b, int nrows) LA_INLINE {
+    // Store outputs of chunk c.  part = I >= 0: row block I (row 16 I + pp
+    // of the chunk, columns 16 cb + 4g .. + 3) in bf16 (OBF) or fp32;
+    // part = -1: den, when asked for.  FULL: all CT rows valid.  The output
+    // type is a template parameter, so on full chunks the stores of the row
+    // blocks need no branch; the den of row block I = wave is written by wave
+    // `wave`, all four lane groups holding the same value.
+    auto store_out = [&](auto full_tag, int c, int nrows, int part, const f32x4 (&outv)[CBW][NB],
+                         const float (&den)[NB]) LA_INLINE {
         constexpr bool FULL = decltype(full_tag)::value;
-        char *buf = smem + b * T::BUF;
-        if (weighted && tid < T::ROWS) reinterpret_cast<float *>(buf + T::OFF_W)[tid] = rw;  // zero past the rows
-        auto keep = [&](int row) { return FULL || row < nrows; };
-        if (NEED_Q) {
+        if constexpr (!NEED_Q) return;
+        if (!has_cols) return;
+        const long crow0 = seg_row0 + (long)c * CT;
+        if (part >= 0) {
+            const int I = part;
+            char *oc = static_cast<char *>(p.o) + crow0 * DV * (OBF ? 2 : 4);
 #pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const int row = rq0 + i * RSQ;
-                if ((CT * VQ) % kThreads == 0 || row < CT) {
-                    uint4 out = phi16(rq[i], 1.0f);
-                    if (!keep(row)) out = make_uint4(0u, 0u, 0u, 0u);
-                    *reinterpret_cast<uint4 *>(buf + T::OFF_Q + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
+            for (int cs = 0; cs < CBW; ++cs) {
+                if (col_ok(cs) && (FULL || 16 * I + pp < nrows)) {
+                    const unsigned off = (unsigned)((16 * I + pp) * DV + 16 * (wave + 4 * cs) + 4 * g);
+                    if constexpr (OBF) *reinterpret_cast<uint2 *>(oc + off * 2) = pack_bf16x4(outv[cs][I]);
+                    else *reinterpret_cast<f32x4 *>(oc + off * 4) = outv[cs][I];
                 }
             }
-        }
-        if (NEED_K) {
-#pragma unroll
-            for (int i = 0; i < NLQ; ++i) {
-                const int row = rq0 + i * RSQ;
-                if ((CT * VQ) % kThreads == 0 || row < CT) {
-                    uint4 out = phi16(rk[i], kscaled ? rks[MODE == MODE_AGG ? i : 0] : 1.0f);
-                    if (!keep(row)) out = make_uint4(0u, 0u, 0u, 0u);
-                    *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NLV; ++i) {
-                const int row = rv0 + i * RSV;
-                if ((CT * VV) % kThreads == 0 || row < CT) {
-                    uint4 out = rv[i];
-                    if (!keep(row)) out = make_uint4(0u, 0u, 0u, 0u);
-                    *reinterpret_cast<uint4 *>(buf + T::OFF_V + lv0 + i * RSV * T::LV * (int)sizeof(TC)) = out;
-                }
-            }
-        }
-    };
-
-    // Compute chunk c from LDS buffer b (FULL: all CT rows valid).  All
-    // matrix work is one straight-line block; the stores come last.
-    auto compute = [&](auto full_tag, int b, int c, int nrows) LA_INLINE {
-        constexpr bool FULL = decltype(full_tag)::value;
-        const char *buf = smem + b * T::BUF;
-        const TC *sq = reinterpret_cast<const TC *>(buf + T::OFF_Q);
-        const TC *sk = reinterpret_cast<const TC *>(buf + T::OFF_K);
-        const TC *sv = reinterpret_cast<const TC *>(buf + T::OFF_V);
-        if (NEED_Q && has_cols) {
-            f32x4 outv[CBW][NB];
-            float den[NB];
-            // V^T(cb) in the split assignment over tokens (A operand of the intra product)
-            Frag<TC> fvt[CBW][NP];
-            if (MODE == MODE_CAUSAL) {
-#pragma unroll
-                for (int cs = 0; cs < CBW; ++cs)
-#pragma unroll
-                    for (int jp = 0; jp < NP; ++jp)
-                        if (wave + 4 * cs < CBT)
-                            lds_frag_tr(fvt[cs][jp], sv, T::LV, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g,
-                                        16 * (wave + 4 * cs), pp);
-            }
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                const TC *qrow = &sq[(16 * I + pp) * T::LQ];
-                Frag<TC> fq[NSE];
-#pragma unroll
-                for (int s = 0; s < NSE; ++s) lds_frag_split(fq[s], qrow + 32 * s, qrow + 32 * s + 16, g);
-                // den_i = phi(q_i) . z + sum_{j <= i} A_ij, both on the matrix
-                // cores: every accumulator slot of lane (i, g) ends up holding den_i.
-                f32x4 accD = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
-                Frag<TC> fb[NP];  // A^T key-block pairs as B operands (split over tokens)
-                if (MODE == MODE_CAUSAL) {
-                    f32x4 accA[2 * NP];
-#pragma unroll
-                    for (int J = 0; J < 2 * NP; ++J) {
-                        accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (J <= I) {
-#pragma unroll
-                            for (int s = 0; s < NSE; ++s) {
-                                Frag<TC> fk;  // phi(K) rows of key block J, split over features
-                                const TC *krow = &sk[(16 * J + pp) * T::LQ + 32 * s];
-                                lds_frag_split(fk, krow, krow + 16, g);
-                                accA[J] = mma(fk, fq[s], accA[J]);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) accA[I][r] = diag_keep[r] ? accA[I][r] : 0.f;  // j <= i
-#pragma unroll
-                    for (int jp = 0; jp < NP; ++jp) {
-                        if (2 * jp <= I) {
-                            acc_to_frag(fb[jp], accA[2 * jp], accA[2 * jp + 1]);
-                            accD = mma(ones, fb[jp], accD);
-                        }
-                    }
-                }
-                den[I] = accD[0];
-                const float inv = __builtin_amdgcn_rcpf(accD[0]);
-#pragma unroll
-                for (int cs = 0; cs < CBW; ++cs) {
-                    if (wave + 4 * cs < CBT) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                        if (MODE == MODE_CAUSAL) {
-#pragma unroll
-                            for (int jp = 0; jp < NP; ++jp)
-                                if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
-                        }
-#pragma unroll
-                        for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
-                        outv[cs][I] = acc * inv;
-                    }
-                }
-            }
-            // stores: row 16 I + pp of the chunk, columns 16 cb + 4g .. + 3
-            const long crow0 = seg_row0 + (long)c * CT;
-            if (p.out_bf16) {
-                char *oc = static_cast<char *>(p.o) + crow0 * DV * 2;
-#pragma unroll
-                for (int cs = 0; cs < CBW; ++cs)
-#pragma unroll
-                    for (int I = 0; I < NB; ++I)
-                        if (wave + 4 * cs < CBT && (FULL || 16 * I + pp < nrows))
-                            *reinterpret_cast<uint2 *>(oc + (unsigned)(((16 * I + pp) * DV + 16 * (wave + 4 * cs) + 4 * g) * 2)) =
-                                pack_bf16x4(outv[cs][I]);
-            } else {
-                char *oc = static_cast<char *>(p.o) + crow0 * DV * 4;
-#pragma unroll
-                for (int cs = 0; cs < CBW; ++cs)
-#pragma unroll
-                    for (int I = 0; I < NB; ++I)
-                        if (wave + 4 * cs < CBT && (FULL || 16 * I + pp < nrows))
-                            *reinterpret_cast<f32x4 *>(oc + (unsigned)(((16 * I + pp) * DV + 16 * (wave + 4 * cs) + 4 * g) * 4)) =
-                                outv[cs][I];
-            }
-            if (p.den && wave == 0 && g == 0) {
+        } else if (p.den) {
+            if constexpr (NB == 4 && CBT % 4 == 0) {
+                // a vector (not the array) is indexed by the wave, so the
+                // array stays in registers
+                const f32x4 dv = {den[0], den[1], den[2], den[3]};
+                const float d = dv[wave];
+                if (FULL || 16 * wave + pp < nrows) p.den[crow0 + 16 * wave + pp] = d;
+            } else if (wave == 0 && g == 0) {
 #pragma unroll
                 for (int I = 0; I < NB; ++I)
                     if (FULL || 16 * I + pp < nrows) p.den[crow0 + 16 * I + pp] = den[I];
             }
         }
+    };
+
+    // Per-lane bases of the split-fragment reads of the q and k tiles (row
+    // pp, slot 4g), one per 32-feature step and half, so that no two of
+    // these reads are merged (see lds_opaque).  Tile offsets are added as
+    // element counts.
+    lds_cptr<TC> fbase[NSE][2];
+#pragma unroll
+    for (int s = 0; s < NSE; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            fbase[s][h] = lds_opaque(reinterpret_cast<const TC *>(smem) + pp * T::LQ + 4 * g + 32 * s + 16 * h);
+
+    // Outputs of one chunk, one row block I at a time (four-wave kernels:
+    // their registers hold one block's operands at a time).
+    auto outputs_by_block = [&](int qoff, int koff, const TC *sv, f32x4 (&outv)[CBW][NB], float (&den)[NB],
+                                auto &&store) LA_INLINE {
+        // V^T(cb) in the split assignment over tokens (A operand of the intra product)
+        Frag<TC> fvt[CBW][NP];
+        if (MODE == MODE_CAUSAL) {
+#pragma unroll
+            for (int cs = 0; cs < CBW; ++cs)
+#pragma unroll
+                for (int jp = 0; jp < NP; ++jp)
+                    if (col_ok(cs))
+                        lds_frag_tr(fvt[cs][jp], sv, T::LV, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g,
+                                    16 * (wave + 4 * cs), pp);
+        }
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            Frag<TC> fq[NSE];
+#pragma unroll
+            for (int s = 0; s < NSE; ++s) lds_frag_split_at(fq[s], fbase[s][0], fbase[s][1], qoff + 16 * I * T::LQ);
+            // den_i = phi(q_i) . z + sum_{j <= i} A_ij, both on the matrix
+            // cores: every accumulator slot of lane (i, g) ends up holding den_i.
+            f32x4 accD = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
+            Frag<TC> fb[NP];  // A^T key-block pairs as B operands (split over tokens)
+            if (MODE == MODE_CAUSAL) {
+                f32x4 accA[2 * NP];
+#pragma unroll
+                for (int J = 0; J < 2 * NP; ++J) {
+                    accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (J <= I) {
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) {
+                            Frag<TC> fk;  // phi(K) rows of key block J, split over features
+                            lds_frag_split_at(fk, fbase[s][0], fbase[s][1], koff + 16 * J * T::LQ);
+                            accA[J] = mma(fk, fq[s], accA[J]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accA[I][r] = diag_keep[r] ? accA[I][r] : 0.f;  // j <= i
+#pragma unroll
+                for (int jp = 0; jp < NP; ++jp) {
+                    if (2 * jp <= I) {
+                        acc_to_frag(fb[jp], accA[2 * jp], accA[2 * jp + 1]);
+                        accD = mma(ones, fb[jp], accD);
+                    }
+                }
+            }
+            den[I] = accD[0];
+            const float inv = __builtin_amdgcn_rcpf(accD[0]);
+#pragma unroll
+            for (int cs = 0; cs < CBW; ++cs) {
+                if (col_ok(cs)) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if (MODE == MODE_CAUSAL) {
+#pragma unroll
+                        for (int jp = 0; jp < NP; ++jp)
+                            if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
+                    }
+#pragma unroll
+                    for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                    outv[cs][I] = acc * inv;
+                }
+            }
+            store(I, outv, den);
+        }
+    };
+
+    // Outputs of one chunk in phases over all row blocks at once (split
+    // kernels, whose compute waves have the registers): every operand read is
+    // issued first, then the row blocks' score tiles and products, so the LDS
+    // latency is paid once per chunk and the matrix-core latencies of one
+    // block hide behind the work of the next.
+    auto outputs_phased = [&](int qoff, int koff, const TC *sv, f32x4 (&outv)[CBW][NB], float (&den)[NB],
+                              auto &&store) LA_INLINE {
+        constexpr bool CAUSAL = MODE == MODE_CAUSAL;
+        Frag<TC> fk[CAUSAL ? NB : 1][NSE];  // phi(K) rows of block J (A operand)
+        Frag<TC> fvt[CBW][NP];           // V^T(cb) over token pairs (A operand)
+        if constexpr (CAUSAL) {
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int s = 0; s < NSE; ++s) lds_frag_split_at(fk[J][s], fbase[s][0], fbase[s][1], koff + 16 * J * T::LQ);
+#pragma unroll
+            for (int cs = 0; cs < CBW; ++cs)
+#pragma unroll
+                for (int jp = 0; jp < NP; ++jp)
+                    if (col_ok(cs))
+                        lds_frag_tr(fvt[cs][jp], sv, T::LV, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g,
+                                    16 * (wave + 4 * cs), pp);
+        }
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            Frag<TC> fq[NSE];  // phi(Q) rows of block I, split over features (B operand)
+#pragma unroll
+            for (int s = 0; s < NSE; ++s) lds_frag_split_at(fq[s], fbase[s][0], fbase[s][1], qoff + 16 * I * T::LQ);
+            // den_i = phi(q_i) . z + sum_{j <= i} A_ij, on the matrix cores:
+            // every accumulator slot of lane (i, g) ends up holding den_i.
+            f32x4 accD = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
+            Frag<TC> fb[NP];  // A^T key-block pairs as B operands (split over tokens)
+            if constexpr (CAUSAL) {
+                // score tiles A^T(J, I) for J <= I
+                f32x4 accA[2 * NP];
+#pragma unroll
+                for (int J = 0; J < 2 * NP; ++J) {
+                    accA[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (J <= I) {
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) accA[J] = mma(fk[J][s], fq[s], accA[J]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accA[I][r] = diag_keep[r] ? accA[I][r] : 0.f;  // j <= i
+#pragma unroll
+                for (int jp = 0; jp < NP; ++jp) {
+                    if (2 * jp <= I) {
+                        acc_to_frag(fb[jp], accA[2 * jp], accA[2 * jp + 1]);
+                        accD = mma(ones, fb[jp], accD);
+                    }
+                }
+            }
+            den[I] = accD[0];
+            const float inv = __builtin_amdgcn_rcpf(accD[0]);
+#pragma unroll
+            for (int cs = 0; cs < CBW; ++cs) {
+                if (col_ok(cs)) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (CAUSAL) {
+#pragma unroll
+                        for (int jp = 0; jp < NP; ++jp)
+                            if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
+                    }
+#pragma unroll
+                    for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                    outv[cs][I] = acc * inv;
+                }
+            }
+            store(I, outv, den);
+        }
+    };
+
+    // Compute the chunk in LDS buffer b: outputs into outv/den, `store(I)`
+    // writes row block I as soon as it is done and `store(-1)` the den, then
+    // the state carry.
+    auto compute = [&](int b, auto &&store) LA_INLINE {
+        const char *buf = smem + b * T::BUF;
+        const int qoff = (b * T::BUF + T::OFF_Q) / (int)sizeof(TC);  // tile offsets in elements
+        const int koff = (b * T::BUF + T::OFF_K) / (int)sizeof(TC);
+        const TC *sk = reinterpret_cast<const TC *>(buf + T::OFF_K);
+        const TC *sv = reinterpret_cast<const TC *>(buf + T::OFF_V);
+        f32x4 outv[CBW][NB];  // outputs of the chunk, held until their stores
+        float den[NB];
+        if constexpr (SPLIT) {
+            if (NEED_Q && has_cols) outputs_phased(qoff, koff, sv, outv, den, store);
+        } else {
+            if (NEED_Q && has_cols) outputs_by_block(qoff, koff, sv, outv, den, store);
+        }
+        store(-1, outv, den);
 
         // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
         if (NEED_K && has_cols) {
@@ -458,86 +640,98 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
             for (int s = 0; s < NP; ++s) {
                 Frag<TC> fkt[NE];
-                // z weights over this step's tokens (straight assignment), as a
+                // z weights over this step's tokens (split assignment), as a
                 // value and its rounding remainder when the operands are bf16
                 Frag<TC> fw = ones, fw_lo;
                 if (weighted) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
-                        const float x = sw[32 * s + 8 * g + t];
+                        const float x = sw[32 * s + (t < 4 ? 4 * g + t : 16 + 4 * g + t - 4)];
                         fw.set(t, x);
                         fw_lo.set(t, x - fw.get(t));
                     }
                 }
 #pragma unroll
                 for (int E = 0; E < NE; ++E) {
-                    lds_frag_tr(fkt[E], sk, T::LQ, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * E, pp);
+                    lds_frag_tr(fkt[E], sk, T::LQ, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * E, pp);
                     accZ[E] = mma(fkt[E], fw, accZ[E]);
                     if (weighted && sizeof(TC) == 2) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
                 }
 #pragma unroll
                 for (int cs = 0; cs < CBW; ++cs) {
                     const int cb = wave + 4 * cs;
-                    if (cb < CBT) {
+                    if (col_ok(cs)) {
                         Frag<TC> fv;
-                        lds_frag_tr(fv, sv, T::LV, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * cb, pp);
+                        lds_frag_tr(fv, sv, T::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cb, pp);
 #pragma unroll
                         for (int E = 0; E < NE; ++E) accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
                     }
                 }
-            }
+                    }
             if (MODE == MODE_CAUSAL) refresh_state_frags();
         }
     };
 
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    auto rows_of = [&](int c) { return min(CT, row_end - row_begin - c * CT); };
-
-    if (nch > 0) {
-        load_any(0);
-        __syncthreads();  // the zero fill is complete before any tile write
-        stage(Part{}, 0, rows_of(0));
-        if (nch > 1) load_any(1);
-        __syncthreads();
-    }
-    int ch = 0;
-    if constexpr (NBUF == 2) {
-        // Steady state, two chunks per trip: chunks ch .. ch + 3 are full.
-        // Stage the next chunk, prefetch the one after, compute this one.
-        for (; ch + 3 < nfull; ch += 2) {
-            stage(Full{}, 1, CT);
-            load_full(ch + 2);
-            compute(Full{}, 0, ch, CT);
-            __syncthreads();
-            stage(Full{}, 0, CT);
-            load_full(ch + 3);
-            compute(Full{}, 1, ch + 1, CT);
-            __syncthreads();
-        }
-        for (; ch < nch; ++ch) {
-            const int b = ch & 1;
-            if (ch + 1 < nch) {
-                stage(Part{}, b ^ 1, rows_of(ch + 1));
-                if (ch + 2 < nch) load_any(ch + 2);
+    if constexpr (SPLIT) {
+        // Compute step j: wait for chunk j, compute it (the barrier before
+        // step j + 2 frees its buffer).
+        __syncthreads();  // zero fill
+        int j = 0;
+        if constexpr (NBUF == 2) {
+            for (; j + 3 < nfull; j += 2) {  // same trip count as the staging waves
+                __syncthreads();
+                compute(0, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
+                __syncthreads();
+                compute(1, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j + 1, CT, part, o, d); });
             }
-            compute(Part{}, b, ch, rows_of(ch));
+        }
+        for (; j < nch; ++j) {
+            const int b = NBUF == 2 ? (j & 1) : 0;
             __syncthreads();
+            if (j < nfull) compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
+            else compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, j, rows_of(j), part, o, d); });
+            if (NBUF == 1 && j + 1 < nch) __syncthreads();  // the staging waves refill the single buffer
         }
     } else {
-        for (; ch + 2 < nfull; ++ch) {
-            compute(Full{}, 0, ch, CT);
-            __syncthreads();
-            stage(Full{}, 0, CT);
-            load_full(ch + 2);
-            __syncthreads();
+        // ---- four waves in both roles: stage chunk c + 1, compute chunk c ----
+        load_any(S0t{}, 0);
+        __syncthreads();  // the zero fill is complete before any tile write
+        stage(S0t{}, Part{}, 0, rows_of(0));
+        load_any(S0t{}, 1);  // clamped rows when there is no chunk 1
+        __syncthreads();
+        int ch = 0;
+        // Full chunks.
+        if constexpr (NBUF == 2) {
+            for (; ch + 2 < nfull; ++ch) {  // chunks ch .. ch + 2 are full
+                const int b = ch & 1;
+                stage(S0t{}, Full{}, b ^ 1, CT);
+                load(S0t{}, Full{}, ch + 2);
+                compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+                __syncthreads();
+            }
+        } else {
+            for (; ch + 2 < nfull; ++ch) {
+                compute(0, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+                __syncthreads();
+                stage(S0t{}, Full{}, 0, CT);
+                load(S0t{}, Full{}, ch + 2);
+                __syncthreads();
+            }
         }
         for (; ch < nch; ++ch) {
-            compute(Part{}, 0, ch, rows_of(ch));
+            const int b = NBUF == 2 ? (ch & 1) : 0;
+            if (NBUF == 2 && ch + 1 < nch) {
+                if (ch + 1 < nfull) stage(S0t{}, Full{}, b ^ 1, CT);
+                else stage(S0t{}, Part{}, b ^ 1, rows_of(ch + 1));
+                if (ch + 2 < nch) load_any(S0t{}, ch + 2);
+            }
+            if (ch < nfull) compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+            else compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, ch, rows_of(ch), part, o, d); });
             __syncthreads();
-            if (ch + 1 < nch) {
-                stage(Part{}, 0, rows_of(ch + 1));
-                if (ch + 2 < nch) load_any(ch + 2);
+            if (NBUF == 1 && ch + 1 < nch) {
+                if (ch + 1 < nfull) stage(S0t{}, Full{}, 0, CT);
+                else stage(S0t{}, Part{}, 0, rows_of(ch + 1));
+                if (ch + 2 < nch) load_any(S0t{}, ch + 2);
                 __syncthreads();
             }
         }
@@ -546,7 +740,7 @@ la_chunk_kernel(const FwdParams p) {
     // ---- write the segment's resulting state ----
     float *Sdst = nullptr;
     float *zdst = nullptr;
-    if (MODE == MODE_AGG) {
+    if (AGGM) {
         Sdst = p.seg_out + (bh * p.state_P + seg) * (long)(DK * DV + DK);
         zdst = Sdst + DK * DV;
     } else if (MODE == MODE_CAUSAL && seg == (int)gridDim.y - 1 && p.S_fin) {
@@ -557,7 +751,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
         for (int cs = 0; cs < CBW; ++cs) {
             const int cb = wave + 4 * cs;
-            if (cb < CBT) {
+            if (col_ok(cs)) {
 #pragma unroll
                 for (int E = 0; E < NE; ++E)
 #pragma unroll

@@ -11,23 +11,24 @@
 namespace la {
 
 // Resident workgroups of one instantiation of the chunk kernel (cached).
-template <int DK, int DV, typename TI, int MODE, int CT>
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false>
 long chunk_resident() {
     static OccCache cache;
-    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT>), cache);
+    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF>), cache,
+                               fwd_threads<DK, DV, TI>());
 }
 
-template <int DK, int DV, typename TI, int CT>
+template <int DK, int DV, typename TI, int CT, bool OBF>
 hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT>;
-    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT>
-                              : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT>;
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT, false>;
+    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF>
+                              : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
     const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT>();
-    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT>()
-                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT>();
+    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF>()
+                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF>();
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
     const long want_main = (target_main + BH - 1) / BH;
@@ -41,7 +42,6 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.o = d.o;
     p.den = d.den;
     p.N = d.N;
-    p.out_bf16 = d.out_bf16;
     p.state_P = Pf;
     hipError_t err;
 
@@ -52,18 +52,18 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
             p.seg_out = d.ws;
             p.L = Lf;
             p.state_mult = 1;
-            agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(p);
+            agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
             p.seg_state = d.ws;
             p.state_mult = mult;
             p.L = Lf * mult;
-            main_kernel<<<dim3((unsigned)BH, (unsigned)Pm), kThreads, 0, d.stream>>>(p);
+            main_kernel<<<dim3((unsigned)BH, (unsigned)Pm), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
         } else {
             p.S0 = d.S0;
             p.z0 = d.z0;
             p.L = d.N;
-            main_kernel<<<dim3((unsigned)BH, 1u), kThreads, 0, d.stream>>>(p);
+            main_kernel<<<dim3((unsigned)BH, 1u), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
         }
         return hipGetLastError();
     }
@@ -71,7 +71,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.seg_out = d.ws;
     p.L = Lf;
     p.state_mult = 1;
-    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), kThreads, 0, d.stream>>>(p);
+    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (Pf > 1) {
         if ((err = launch_seg_scan(d.ws, nullptr, nullptr, BH, Pf, DK, DV, 1, d.stream)) != hipSuccess) return err;
@@ -81,7 +81,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const int Pa = plan_segments(BH, d.N, d.C, target_main, &La);
     p.seg_state = d.ws;
     p.L = La;
-    main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), kThreads, 0, d.stream>>>(p);
+    main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
     return hipGetLastError();
 }
 
@@ -95,10 +95,11 @@ template <int DK, int DV, typename TI> constexpr int fwd_chunk(int C) {
 
 template <int DK, int DV, typename TI>
 hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
+    const bool obf = d.out_bf16 != 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
-        case 16: return run_fwd_ct<DK, DV, TI, 16>(d, causal);
-        case 32: return run_fwd_ct<DK, DV, TI, 32>(d, causal);
-        case 64: return run_fwd_ct<DK, DV, TI, 64>(d, causal);
+        case 16: return obf ? run_fwd_ct<DK, DV, TI, 16, true>(d, causal) : run_fwd_ct<DK, DV, TI, 16, false>(d, causal);
+        case 32: return obf ? run_fwd_ct<DK, DV, TI, 32, true>(d, causal) : run_fwd_ct<DK, DV, TI, 32, false>(d, causal);
+        case 64: return obf ? run_fwd_ct<DK, DV, TI, 64, true>(d, causal) : run_fwd_ct<DK, DV, TI, 64, false>(d, causal);
         default: return hipErrorInvalidValue;
     }
 }
