@@ -229,32 +229,32 @@ la_chunk_kernel(const FwdParams p) {
                 };
                 if (NEED_Q) {
 #pragma unroll
-                    for (int i = 0; i < NLQ; ++i) rq[S][i] = *reinterpret_cast<const uint4 *>(qc + offq(i));
+                    for (int i = 0; i < NLQ; ++i) rq[S][i] = load_stream16(qc + offq(i));
                 }
                 if (NEED_K) {
 #pragma unroll
-                    for (int i = 0; i < NLQ; ++i) rk[S][i] = *reinterpret_cast<const uint4 *>(kc + offq(i));
+                    for (int i = 0; i < NLQ; ++i) rk[S][i] = load_stream16(kc + offq(i));
 #pragma unroll
-                    for (int i = 0; i < NLV; ++i) rv[S][i] = *reinterpret_cast<const uint4 *>(vc + offv(i));
+                    for (int i = 0; i < NLV; ++i) rv[S][i] = load_stream16(vc + offv(i));
                 }
             } else {
                 if (NEED_Q) {
 #pragma unroll
                     for (int i = 0; i < NLQ; ++i) {
                         const long row = min(r0 + rq0 + i * RSQ, last);
-                        rq[S][i] = *reinterpret_cast<const uint4 *>(qs + (row * DK + cq0) * (long)sizeof(TI));
+                        rq[S][i] = load_stream16(qs + (row * DK + cq0) * (long)sizeof(TI));
                     }
                 }
                 if (NEED_K) {
 #pragma unroll
                     for (int i = 0; i < NLQ; ++i) {
                         const long row = min(r0 + rq0 + i * RSQ, last);
-                        rk[S][i] = *reinterpret_cast<const uint4 *>(ks + (row * DK + cq0) * (long)sizeof(TI));
+                        rk[S][i] = load_stream16(ks + (row * DK + cq0) * (long)sizeof(TI));
                     }
 #pragma unroll
                     for (int i = 0; i < NLV; ++i) {
                         const long row = min(r0 + rv0 + i * RSV, last);
-                        rv[S][i] = *reinterpret_cast<const uint4 *>(vs + (row * DV + cv0) * (long)sizeof(TI));
+                        rv[S][i] = load_stream16(vs + (row * DV + cv0) * (long)sizeof(TI));
                     }
                 }
             }
