@@ -32,20 +32,29 @@
 // and the suffix state is R = sum_i (phi(q_i) a_i) g_i^T, r = sum_i (phi(q_i) a_i) e_i,
 // so R v_j + r sums the same brackets g_i . v_j + e_i.
 //
-// Workgroups have eight waves.  In the dq sweep wave w owns the feature
-// blocks eb = w, w + 8, ... of dq and its slice S[eb, :] of the state, held
-// as accumulators of S^T so it feeds the matrix cores as an operand over the
-// value index.  In the dk/dv sweep wave w owns the feature blocks of dk with
-// R[eb, :] in accumulators, and the value blocks of dv; the dv product needs R
-// contracted over features, so a bf16 copy of R is kept in LDS and read with
-// the transpose read.
+// Workgroups have eight waves; the next chunk's rows are loaded into
+// registers while the current chunk is computed.  Per chunk, the token-pair
+// products (M, and A in the dk/dv sweep) are formed once, one 16 x 16 block
+// per wave, and handed to every wave through LDS.  The feature-dimension work
+// is split by blocks of 16: in the dq sweep wave w owns feature block w of dq
+// and the rows S[16w.., :] of the state, held as accumulators of S^T so that
+// they feed the matrix cores as an operand over the value index; in the dk/dv
+// sweep wave w owns feature block w of dk with R[16w.., :] in accumulators,
+// and value block w of dv, which needs R contracted over features: a copy of
+// R in LDS, read with the transpose read.
+//
+// LDS row strides: tiles read row-wise (two 8-byte pieces per lane, rows p =
+// 0..15) are padded to a stride of 4 (mod 8) times an odd number of banks,
+// tiles read with the transpose read (rows 4g..4g+3 per lane group) to 8
+// times an odd number; each pattern is then free of bank conflicts.
 #pragma once
 
 #include "la_device.hpp"
 
 namespace la {
 
-constexpr int kBwdThreads = 512;  // eight waves
+constexpr int kBwdThreads = 512;
+constexpr int kBwdWaves = 8;
 
 struct BwdParams {
     const void *q, *k, *v;
@@ -64,52 +73,80 @@ template <typename TI, int DK, int DV> constexpr int bwd_cmax() {
     return (sizeof(TI) == 4 && (DK > 64 || DV > 64)) ? 32 : 64;
 }
 
-// Row-major tiles of one chunk in LDS (padding keeps 16-byte alignment).
-template <typename TC> struct BwdTile {
-    static constexpr int PAD = 16 / sizeof(TC);
+// Leading dimensions (elements) of a tile of D columns (padded to >= 32).
+template <typename TC, int D> struct BwdLd {
+    static constexpr int DP = D < 32 ? 32 : D;
+    static constexpr int ROW = DP + (sizeof(TC) == 2 ? 8 : 4);  // row-wise reads
+    static constexpr int TR = DP + (sizeof(TC) == 2 ? 16 : 4);  // transpose reads
 };
 
-// Stage one chunk of rows [r0, r0 + nrows) of a [N][D] tensor into a tile,
-// optionally through phi or times a per-row factor.  Rows past nrows are zero.
-template <typename TI, int D, int LD, int NT>
-__device__ __forceinline__ void bwd_stage(const void *src, long row_base, int r0, int nrows, int C, TI *tile,
-                                          int tid, int how /*0 raw, 1 phi, 3 times row_scale*/,
-                                          const float *row_scale = nullptr) {
-    constexpr int VEC = Store<TI>::VEC;
-    constexpr int VPR = D / VEC;
-    for (int idx = tid; idx < C * VPR; idx += NT) {
-        const int row = idx / VPR;
-        const int col = (idx % VPR) * VEC;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (row < nrows)
-            u = *reinterpret_cast<const uint4 *>(static_cast<const char *>(src) +
-                                                 ((row_base + r0 + row) * D + col) * (long)sizeof(TI));
-        if (how == 0 || row >= nrows) {
-            *reinterpret_cast<uint4 *>(tile + row * LD + col) = u;
-        } else {
-            float x[VEC];
-            unpack16(u, x, TI());
-            Frag<TI> w;
-            const float sc = how == 3 ? row_scale[row] : 1.0f;
+// Block b of the lower triangle of a 4 x 4 block grid, row by row:
+// (0,0), (1,0), (1,1), (2,0), ...
+__device__ __forceinline__ void lower_block(int b, int &I, int &J) {
+    I = (b >= 1) + (b >= 3) + (b >= 6);
+    J = b - I * (I + 1) / 2;
+}
+
+// One chunk of rows of a [N][D] tensor held in registers between its global
+// load and its LDS store, so that the loads of chunk c + 1 are in flight while
+// chunk c is computed.  Every lane issues the same number of loads (rows past
+// the chunk's end are clamped to its last row and zeroed at the store), which
+// keeps the wait before the store exact.
+template <typename TI, int D, int NT, int CM> struct RowRegs {
+    static constexpr int VEC = Store<TI>::VEC;
+    static constexpr int VPR = D / VEC;  // 16-byte vectors per row
+    static constexpr int NV = CM * VPR;
+    static constexpr int NIT = (NV + NT - 1) / NT;
+    uint4 u[NIT];
+
+    __device__ __forceinline__ void load(const void *src, long row_base, int r0, int nrows, int tid) {
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) w.set(t, how == 1 ? phi(x[t]) : x[t] * sc);
-            if constexpr (sizeof(TI) == 2) {
-                *reinterpret_cast<uint4 *>(tile + row * LD + col) = __builtin_bit_cast(uint4, w.v);
-            } else {
-                f32x4 w4 = {w.get(0), w.get(1), w.get(2), w.get(3)};
-                *reinterpret_cast<f32x4 *>(tile + row * LD + col) = w4;
-            }
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = tid + it * NT;
+            const int row = min(idx / VPR, nrows - 1);
+            const int col = (idx % VPR) * VEC;
+            u[it] = load_stream16(static_cast<const char *>(src) +
+                                  ((row_base + r0 + row) * D + col) * (long)sizeof(TI));
         }
     }
-}
+
+    // Rows [0, CM) of the tile (leading dimension LD): phi of the loaded
+    // values (with_phi) or the values themselves; zero past nrows.
+    template <int LD>
+    __device__ __forceinline__ void store(TI *tile, int nrows, int tid, bool with_phi) const {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int idx = tid + it * NT;
+            if (NV % NT != 0 && idx >= NV) continue;
+            const int row = idx / VPR;
+            const int col = (idx % VPR) * VEC;
+            uint4 w = make_uint4(0, 0, 0, 0);
+            if (row < nrows) {
+                if (!with_phi) {
+                    w = u[it];
+                } else {
+                    float x[VEC];
+                    unpack16(u[it], x, TI());
+                    if constexpr (sizeof(TI) == 2) {
+                        const f32x4 a = {phi(x[0]), phi(x[1]), phi(x[2]), phi(x[3])};
+                        const f32x4 b = {phi(x[4]), phi(x[5]), phi(x[6]), phi(x[7])};
+                        const uint2 pa = pack_bf16x4(a), pb = pack_bf16x4(b);
+                        w = make_uint4(pa.x, pa.y, pb.x, pb.y);
+                    } else {
+                        w = make_uint4(__float_as_uint(phi(x[0])), __float_as_uint(phi(x[1])),
+                                       __float_as_uint(phi(x[2])), __float_as_uint(phi(x[3])));
+                    }
+                }
+            }
+            *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
+        }
+    }
+};
 
 template <typename TI>
 __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
     if constexpr (sizeof(TI) == 2) {
-        uint2 w;
-        w.x = (uint32_t)f32_to_bf16_bits(a[0]) | ((uint32_t)f32_to_bf16_bits(a[1]) << 16);
-        w.y = (uint32_t)f32_to_bf16_bits(a[2]) | ((uint32_t)f32_to_bf16_bits(a[3]) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + idx) = w;
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + idx) = pack_bf16x4(a);
     } else {
         *reinterpret_cast<f32x4 *>(static_cast<float *>(dst) + idx) = a;
     }
@@ -120,15 +157,19 @@ __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV, typename TI> struct DqSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
-    static constexpr int DKP = DK < 32 ? 32 : DK;
-    static constexpr int DVP = DV < 32 ? 32 : DV;
-    static constexpr int LK = DKP + BwdTile<TI>::PAD;
-    static constexpr int LV = DVP + BwdTile<TI>::PAD;
-    TI k[CM * LK];    // phi(K)
-    TI q[CM * LK];    // phi(Q)
-    TI v[CM * LV];    // V
-    TI g[CM * LV];    // dO
-    float red[kBwdThreads / 64][64][2];  // per-wave partial phi(q).X and phi(q).z
+    static constexpr int LK = BwdLd<TI, DK>::TR;   // phi(K): transpose reads
+    static constexpr int LQ = BwdLd<TI, DK>::ROW;  // phi(Q): row reads
+    static constexpr int LV = BwdLd<TI, DV>::TR;   // V: transpose reads (state), row reads (M)
+    static constexpr int LG = BwdLd<TI, DV>::ROW;  // dO: row reads
+    static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[i][j]
+    static constexpr bool LO = sizeof(TI) == 2;     // M kept as value + remainder
+    alignas(16) TI k[CM * LK];
+    alignas(16) TI q[CM * LQ];
+    alignas(16) TI v[CM * LV];
+    alignas(16) TI g[CM * LG];
+    alignas(16) TI mh[CM * LM];
+    alignas(16) TI ml[LO ? CM * LM : 4];
+    alignas(16) float red[kBwdWaves][CM][2];  // per-wave partial phi(q).X and phi(q).z
 };
 
 template <int DK, int DV, typename TI>
@@ -136,12 +177,14 @@ __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dq_kernel(const BwdParams p) {
     using TC = TI;
     using SM = DqSmem<DK, DV, TI>;
-    constexpr int NW = kBwdThreads / 64;
-    constexpr int EB = DK / 16, EBW = (EB + NW - 1) / NW;
-    constexpr int NWA = EB < NW ? EB : NW;     // waves holding feature blocks
-    constexpr int CV = DV / 16;                // value tiles of the state
-    constexpr int NSV = (DV + 31) / 32;        // value K steps
-    __shared__ alignas(16) SM sm;
+    constexpr int NW = kBwdWaves;
+    constexpr int EB = DK / 16;          // feature blocks, one per wave
+    constexpr int CV = DV / 16;          // value tiles of the state
+    constexpr int NSV = (DV + 31) / 32;  // value K steps
+    constexpr int NIB = SM::CM / 16;     // 16-row blocks of a full chunk
+    constexpr int NTS = SM::CM / 32;     // 32-token K steps of a full chunk
+    static_assert(EB <= NW, "one feature block per wave");
+    __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, pp = lane & 15;
     const long bh = blockIdx.x;
@@ -152,127 +195,134 @@ la_bwd_dq_kernel(const BwdParams p) {
     const int nch = (row_end - row_begin + C - 1) / C;
     const int nib = C / 16, nts = (C + 31) / 32;
     const bool active = wave < EB;
+    const int eb = wave;
 
     {
         uint32_t *w = reinterpret_cast<uint32_t *>(&sm);
         for (int i = tid; i < (int)(sizeof(SM) / 4); i += kBwdThreads) w[i] = 0u;
     }
 
-    const float *Sin = p.state ? p.state + (bh * p.state_P + (long)seg * p.state_mult) * (long)(DK * DV + DK) : nullptr;
-    const float *zin = Sin ? Sin + DK * DV : nullptr;
     // S^T(c', eb) tiles: lane (pp, g) holds S[16 eb + pp][16 c' + 4g + r]; z(eb): z[16 eb + 4g + r].
-    f32x4 accS[CV][EBW];
-    f32x4 accZ[EBW];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 accS[CV];
+    f32x4 accZ = zero4;
 #pragma unroll
-    for (int es = 0; es < EBW; ++es) {
-        const int eb = wave + NW * es;
+    for (int cv = 0; cv < CV; ++cv) accS[cv] = zero4;
+    if (p.state && active) {
+        const float *Sin = p.state + (bh * p.state_P + (long)seg * p.state_mult) * (long)(DK * DV + DK);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accZ[es][r] = (zin && eb < EB) ? zin[16 * eb + 4 * g + r] : 0.f;
+        for (int r = 0; r < 4; ++r) accZ[r] = Sin[DK * DV + 16 * eb + 4 * g + r];
 #pragma unroll
         for (int cv = 0; cv < CV; ++cv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                accS[cv][es][r] = (Sin && eb < EB) ? Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r] : 0.f;
+            for (int r = 0; r < 4; ++r) accS[cv][r] = Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
     }
-    Frag<TC> fragS[EBW][NSV];  // S rows e, split over the value index
+    Frag<TC> fragS[NSV];  // S rows e, split over the value index
     auto refresh = [&]() {
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int es = 0; es < EBW; ++es)
-#pragma unroll
-            for (int s = 0; s < NSV; ++s)
-                acc_to_frag(fragS[es][s], accS[2 * s][es], (2 * s + 1 < CV) ? accS[2 * s + 1][es] : zero4);
+        for (int s = 0; s < NSV; ++s)
+            acc_to_frag(fragS[s], accS[2 * s], (2 * s + 1 < CV) ? accS[2 * s + 1] : zero4);
     };
     refresh();
     Frag<TC> ones;
     frag_ones(ones);
 
+    RowRegs<TI, DK, kBwdThreads, SM::CM> xk, xq;
+    RowRegs<TI, DV, kBwdThreads, SM::CM> xv, xg;
+    auto fetch = [&](int ch) {
+        const int r0 = row_begin + ch * C;
+        const int nrows = min(C, row_end - r0);
+        xk.load(p.k, bh * N, r0, nrows, tid);
+        xq.load(p.q, bh * N, r0, nrows, tid);
+        xv.load(p.v, bh * N, r0, nrows, tid);
+        xg.load(p.g, bh * N, r0, nrows, tid);
+    };
+    if (nch > 0) fetch(0);
+
+    // per-lane bases of the row-wise reads: row pp, column 4g
+    const lds_vptr<TC> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
+    const lds_vptr<TC> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
+    const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 16 * eb + 4 * g);
+    const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
+    const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
+
     for (int ch = 0; ch < nch; ++ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
+        __syncthreads();  // previous chunk's tile reads done
+        xk.template store<SM::LK>(sm.k, nrows, tid, true);
+        xq.template store<SM::LQ>(sm.q, nrows, tid, true);
+        xv.template store<SM::LV>(sm.v, nrows, tid, false);
+        xg.template store<SM::LG>(sm.g, nrows, tid, false);
         __syncthreads();
-        bwd_stage<TI, DK, SM::LK, kBwdThreads>(p.k, bh * N, r0, nrows, C, sm.k, tid, 1);
-        bwd_stage<TI, DK, SM::LK, kBwdThreads>(p.q, bh * N, r0, nrows, C, sm.q, tid, 1);
-        bwd_stage<TI, DV, SM::LV, kBwdThreads>(p.v, bh * N, r0, nrows, C, sm.v, tid, 0);
-        bwd_stage<TI, DV, SM::LV, kBwdThreads>(p.g, bh * N, r0, nrows, C, sm.g, tid, 0);
+        if (ch + 1 < nch) fetch(ch + 1);
+
+        // Masked M_ij = g_i . v_j (j <= i) over the blocks I >= J, one block
+        // per wave and pass; blocks above the diagonal stay zero in LDS.
+        for (int b = wave; b < nib * (nib + 1) / 2; b += NW) {
+            int I, J;
+            lower_block(b, I, J);
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int s = 0; s < NSV; ++s) {
+                Frag<TC> fv, fg;
+                lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
+                lds_frag_split_v(fg, gb, 16 * I * SM::LG + 32 * s);
+                acc = mma(fv, fg, acc);
+            }
+            // lane: tokens j = 16 J + 4g + r of query i = 16 I + pp
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (I == J && 4 * g + r > pp) acc[r] = 0.f;
+            const int off = (16 * I + pp) * SM::LM + 16 * J + 4 * g;
+            lds_put4_pair(sm.mh + off, sm.ml + (SM::LO ? off : 0), acc);
+        }
         __syncthreads();
 
-        // X(eb, I) = sum_{j<=i} (v_j . g_i) phi(k_j) + S g_i and Z(eb, I) = z_i,
-        // both with rows e = 16 eb + 4g + r of query column i = 16 I + pp.
-        f32x4 X[4][EBW], Z[4][EBW];
+        // X(eb, I) = sum_{j<=i} M_ij phi(k_j) + S g_i and Z(eb, I) = z_i, both
+        // with rows e = 16 eb + 4g + r of query column i = 16 I + pp.
+        f32x4 X[NIB], Z[NIB];
+        Frag<TC> fkt[NTS];  // phi(K) over tokens (split), features 16 eb + pp
         if (active) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int jp = 0; jp < NTS; ++jp)
+                lds_frag_tr(fkt[jp], sm.k, SM::LK, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g, 16 * eb, pp);
+#pragma unroll
+            for (int I = 0; I < NIB; ++I) {
+                X[I] = zero4;
+                Z[I] = zero4;
                 if (I < nib) {
                     Frag<TC> fg[NSV];
-                    const TC *grow = &sm.g[(16 * I + pp) * SM::LV];
 #pragma unroll
-                    for (int s = 0; s < NSV; ++s) lds_frag_split(fg[s], grow + 32 * s, grow + 32 * s + 16, g);
-                    f32x4 accM[4];
+                    for (int s = 0; s < NSV; ++s) lds_frag_split_v(fg[s], gb, 16 * I * SM::LG + 32 * s);
+                    f32x4 ax = zero4, az = accZ;
 #pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        accM[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (J <= I) {
-                            const TC *vrow = &sm.v[(16 * J + pp) * SM::LV];
-#pragma unroll
-                            for (int s = 0; s < NSV; ++s) {
-                                Frag<TC> fv;
-                                lds_frag_split(fv, vrow + 32 * s, vrow + 32 * s + 16, g);
-                                accM[J] = mma(fv, fg[s], accM[J]);
-                            }
-                            if (J == I) {
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    if (4 * g + r > pp) accM[J][r] = 0.f;  // j <= i
-                            }
-                        }
-                    }
-                    // masked scores as operand value + remainder, and the causal
-                    // all-ones mask over the same tokens
-                    Frag<TC> fb[2], fbl[2], ftr[2];
-#pragma unroll
-                    for (int jp = 0; jp < 2; ++jp) {
+                    for (int jp = 0; jp < NTS; ++jp) {
                         if (2 * jp <= I) {
-                            acc_to_frag(fb[jp], accM[2 * jp], accM[2 * jp + 1]);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) {
-                                fbl[jp].set(t, accM[2 * jp][t] - fb[jp].get(t));
-                                fbl[jp].set(t + 4, accM[2 * jp + 1][t] - fb[jp].get(t + 4));
-                                const int j0 = 32 * jp + 4 * g + t, j1 = j0 + 16, i = 16 * I + pp;
-                                ftr[jp].set(t, j0 <= i ? 1.f : 0.f);
-                                ftr[jp].set(t + 4, j1 <= i ? 1.f : 0.f);
+                            Frag<TC> fm, ftr;
+                            lds_frag_split_v(fm, mhb, 16 * I * SM::LM + 32 * jp);
+                            ax = mma(fkt[jp], fm, ax);
+                            if constexpr (SM::LO) {
+                                lds_frag_split_v(fm, mlb, 16 * I * SM::LM + 32 * jp);
+                                ax = mma(fkt[jp], fm, ax);
                             }
+                            const int i = 16 * I + pp;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) {  // causal all-ones mask over the same tokens
+                                ftr.set(t, 32 * jp + 4 * g + t <= i ? 1.f : 0.f);
+                                ftr.set(t + 4, 32 * jp + 16 + 4 * g + t <= i ? 1.f : 0.f);
+                            }
+                            az = mma(fkt[jp], ftr, az);
                         }
                     }
+#pragma unroll
+                    for (int s = 0; s < NSV; ++s) ax = mma(fragS[s], fg[s], ax);
+                    const f32x4 fq = lds_get4(qb, 16 * I * SM::LQ);
                     float px = 0.f, pz = 0.f;
-                    const TC *qrow = &sm.q[(16 * I + pp) * SM::LK];
 #pragma unroll
-                    for (int es = 0; es < EBW; ++es) {
-                        const int eb = wave + NW * es;
-                        f32x4 ax = {0.f, 0.f, 0.f, 0.f};
-                        f32x4 az = accZ[es];
-                        if (eb < EB) {
-#pragma unroll
-                            for (int jp = 0; jp < 2; ++jp) {
-                                if (2 * jp <= I) {
-                                    Frag<TC> fkt;
-                                    lds_frag_tr(fkt, sm.k, SM::LK, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g, 16 * eb, pp);
-                                    ax = mma(fkt, fb[jp], ax);
-                                    if (sizeof(TC) == 2) ax = mma(fkt, fbl[jp], ax);
-                                    az = mma(fkt, ftr[jp], az);
-                                }
-                            }
-#pragma unroll
-                            for (int s = 0; s < NSV; ++s) ax = mma(fragS[es][s], fg[s], ax);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float fq = static_cast<float>(qrow[16 * eb + 4 * g + r]);
-                                px += fq * ax[r];
-                                pz += fq * az[r];
-                            }
-                        }
-                        X[I][es] = ax;
-                        Z[I][es] = az;
+                    for (int r = 0; r < 4; ++r) {
+                        px += fq[r] * ax[r];
+                        pz += fq[r] * az[r];
                     }
                     px = sum_over_groups(px);
                     pz = sum_over_groups(pz);
@@ -280,18 +330,20 @@ la_bwd_dq_kernel(const BwdParams p) {
                         sm.red[wave][16 * I + pp][0] = px;
                         sm.red[wave][16 * I + pp][1] = pz;
                     }
+                    X[I] = ax;
+                    Z[I] = az;
                 }
             }
         }
         __syncthreads();  // partial dot products of every wave are in LDS
         if (active) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int I = 0; I < NIB; ++I) {
                 if (I < nib) {
                     const int row_local = 16 * I + pp;
                     float t = 0.f, den = 0.f;
 #pragma unroll
-                    for (int w = 0; w < NWA; ++w) {
+                    for (int w = 0; w < EB; ++w) {
                         t += sm.red[w][row_local][0];
                         den += sm.red[w][row_local][1];
                     }
@@ -303,42 +355,24 @@ la_bwd_dq_kernel(const BwdParams p) {
                         p.inv_den[orow] = inv;
                         p.eps[orow] = -coef;
                     }
-                    const TC *qrow = &sm.q[row_local * SM::LK];
+                    const f32x4 fq = lds_get4(qb, 16 * I * SM::LQ);
+                    f32x4 out;
 #pragma unroll
-                    for (int es = 0; es < EBW; ++es) {
-                        const int eb = wave + NW * es;
-                        if (eb < EB) {
-                            f32x4 out;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float dphi_q = fminf(static_cast<float>(qrow[16 * eb + 4 * g + r]), 1.0f);
-                                out[r] = (X[I][es][r] - Z[I][es][r] * coef) * inv * dphi_q;
-                            }
-                            if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
-                        }
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        out[r] = (X[I][r] - Z[I][r] * coef) * inv * fminf(fq[r], 1.0f);
+                    if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
                 }
             }
             // state carry: S^T(c', eb) += V^T(c') phi(K)(eb), z(eb) += phi(K)(eb)^T 1
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < NTS; ++s) {
                 if (s < nts) {
-                    Frag<TC> fk[EBW];
-#pragma unroll
-                    for (int es = 0; es < EBW; ++es) {
-                        const int eb = wave + NW * es;
-                        if (eb < EB) {
-                            lds_frag_tr(fk[es], sm.k, SM::LK, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * eb, pp);
-                            accZ[es] = mma(fk[es], ones, accZ[es]);
-                        }
-                    }
+                    accZ = mma(fkt[s], ones, accZ);
 #pragma unroll
                     for (int cv = 0; cv < CV; ++cv) {
                         Frag<TC> fvt;
-                        lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * cv, pp);
-#pragma unroll
-                        for (int es = 0; es < EBW; ++es)
-                            if (wave + NW * es < EB) accS[cv][es] = mma(fvt, fk[es], accS[cv][es]);
+                        lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
+                        accS[cv] = mma(fvt, fkt[s], accS[cv]);
                     }
                 }
             }
@@ -352,19 +386,24 @@ la_bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV, typename TI> struct DkvSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
-    static constexpr int DKP = DK < 32 ? 32 : DK;
-    static constexpr int DVP = DV < 32 ? 32 : DV;
-    static constexpr int LK = DKP + BwdTile<TI>::PAD;
-    static constexpr int LV = DVP + BwdTile<TI>::PAD;
-    static constexpr int LR = DV + BwdTile<TI>::PAD;
-    static constexpr int RROWS = DKP;
-    TI q[CM * LK];     // phi(Q)
-    TI k[CM * LK];     // phi(K)
-    TI v[CM * LV];     // V
-    TI g[CM * LV];     // dO
-    TI R[RROWS * LR];  // copy of the suffix state R[e][c'] for the dv product
-    float e[64];       // e = eps * den
-    float a[64];       // a = 1 / den
+    static constexpr int LQ = BwdLd<TI, DK>::TR;   // phi(Q): transpose reads (dk, state), row reads (A)
+    static constexpr int LK = BwdLd<TI, DK>::ROW;  // phi(K): row reads
+    static constexpr int LV = BwdLd<TI, DV>::ROW;  // V: row reads
+    static constexpr int LG = BwdLd<TI, DV>::TR;   // dO: transpose reads (dv, state), row reads (M)
+    static constexpr int LR = BwdLd<TI, DV>::TR;   // R[e][c']: transpose reads
+    static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[j][i], A[j][i]
+    static constexpr int RROWS = DK < 32 ? 32 : DK;
+    static constexpr bool LO = sizeof(TI) == 2;
+    alignas(16) TI q[CM * LQ];
+    alignas(16) TI k[CM * LK];
+    alignas(16) TI v[CM * LV];
+    alignas(16) TI g[CM * LG];
+    alignas(16) TI R[RROWS * LR];  // copy of the suffix state R[e][c'] for the dv product
+    alignas(16) TI mh[CM * LM];
+    alignas(16) TI ml[LO ? CM * LM : 4];
+    alignas(16) TI at[CM * LM];
+    alignas(16) float e[CM];  // e = eps * den
+    alignas(16) float a[CM];  // a = 1 / den
 };
 
 template <int DK, int DV, typename TI>
@@ -372,13 +411,14 @@ __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dkdv_kernel(const BwdParams p) {
     using TC = TI;
     using SM = DkvSmem<DK, DV, TI>;
-    constexpr int NW = kBwdThreads / 64;
-    constexpr int EB = DK / 16, EBW = (EB + NW - 1) / NW;
-    constexpr int CB = DV / 16, CBW = (CB + NW - 1) / NW;
-    constexpr int CV = DV / 16;
+    constexpr int NW = kBwdWaves;
+    constexpr int EB = DK / 16, CB = DV / 16, CV = DV / 16;
     constexpr int NSV = (DV + 31) / 32;
     constexpr int NSE = (DK + 31) / 32;
-    __shared__ alignas(16) SM sm;
+    constexpr int NIB = SM::CM / 16;
+    constexpr int NTS = SM::CM / 32;
+    static_assert(EB <= NW && CB <= NW, "one feature block and one value block per wave");
+    __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, pp = lane & 15;
     const long bh = blockIdx.x;
@@ -388,6 +428,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + C - 1) / C;
     const int nib = C / 16, nts = (C + 31) / 32;
+    const bool has_e = wave < EB, has_c = wave < CB;
+    const int eb = wave, cb = wave;
 
     {
         uint32_t *w = reinterpret_cast<uint32_t *>(&sm);
@@ -395,221 +437,221 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     }
     __syncthreads();
 
-    // Suffix state after this segment: the exclusive suffix of its last fine segment.
-    const float *Rin = nullptr;
-    if (p.state) {
-        const long last = min((long)(seg + 1) * p.state_mult, (long)p.state_P) - 1;
-        Rin = p.state + (bh * p.state_P + last) * (long)(DK * DV + DK);
-    }
-    const float *rin = Rin ? Rin + DK * DV : nullptr;
     // R^T(c', eb) tiles: lane (pp, g) holds R[16 eb + pp][16 c' + 4g + r]; r(eb): r[16 eb + 4g + r].
-    f32x4 accR[CV][EBW];
-    f32x4 accr[EBW];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 accR[CV];
+    f32x4 accr = zero4;
 #pragma unroll
-    for (int es = 0; es < EBW; ++es) {
-        const int eb = wave + NW * es;
+    for (int cv = 0; cv < CV; ++cv) accR[cv] = zero4;
+    if (p.state && has_e) {
+        // suffix state after this segment: the exclusive suffix of its last fine segment
+        const long last = min((long)(seg + 1) * p.state_mult, (long)p.state_P) - 1;
+        const float *Rin = p.state + (bh * p.state_P + last) * (long)(DK * DV + DK);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accr[es][r] = (rin && eb < EB) ? rin[16 * eb + 4 * g + r] : 0.f;
+        for (int r = 0; r < 4; ++r) accr[r] = Rin[DK * DV + 16 * eb + 4 * g + r];
 #pragma unroll
         for (int cv = 0; cv < CV; ++cv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                accR[cv][es][r] = (Rin && eb < EB) ? Rin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r] : 0.f;
+            for (int r = 0; r < 4; ++r) accR[cv][r] = Rin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
     }
-    Frag<TC> fragR[EBW][NSV];  // R rows e, split over the value index
+    Frag<TC> fragR[NSV];  // R rows e, split over the value index
     auto refresh = [&]() {
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int es = 0; es < EBW; ++es) {
-            const int eb = wave + NW * es;
+        for (int s = 0; s < NSV; ++s)
+            acc_to_frag(fragR[s], accR[2 * s], (2 * s + 1 < CV) ? accR[2 * s + 1] : zero4);
 #pragma unroll
-            for (int s = 0; s < NSV; ++s)
-                acc_to_frag(fragR[es][s], accR[2 * s][es], (2 * s + 1 < CV) ? accR[2 * s + 1][es] : zero4);
-            if (eb < EB) {
-                // bf16 / fp32 copy of R rows 16 eb + pp into LDS (row-major [e][c'])
-#pragma unroll
-                for (int cv = 0; cv < CV; ++cv) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sm.R[(16 * eb + pp) * SM::LR + 16 * cv + 4 * g + r] = static_cast<TC>(accR[cv][es][r]);
-                }
-            }
+        for (int cv = 0; cv < CV; ++cv) lds_put4(&sm.R[(16 * eb + pp) * SM::LR + 16 * cv + 4 * g], accR[cv]);
+    };
+    if (has_e) refresh();
+
+    RowRegs<TI, DK, kBwdThreads, SM::CM> xq, xk;
+    RowRegs<TI, DV, kBwdThreads, SM::CM> xv, xg;
+    float xe = 0.f, xa = 0.f;  // e and a of token tid (tid < CM)
+    auto fetch = [&](int ch) {
+        const int r0 = row_begin + ch * C;
+        const int nrows = min(C, row_end - r0);
+        xq.load(p.q, bh * N, r0, nrows, tid);
+        xk.load(p.k, bh * N, r0, nrows, tid);
+        xv.load(p.v, bh * N, r0, nrows, tid);
+        xg.load(p.g, bh * N, r0, nrows, tid);
+        if (tid < SM::CM) {
+            const long t = bh * N + r0 + min(tid, nrows - 1);
+            xe = p.eps[t];
+            xa = p.inv_den[t];
         }
     };
-    refresh();
-    Frag<TC> ones;
-    frag_ones(ones);
+    if (nch > 0) fetch(nch - 1);
+
+    // per-lane bases of the row-wise reads: row pp, column 4g
+    const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 4 * g);
+    const lds_vptr<TC> kb = lds_v(sm.k + pp * SM::LK + 4 * g);
+    const lds_vptr<TC> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
+    const lds_vptr<TC> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
+    const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
+    const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
+    const lds_vptr<TC> atb = lds_v(sm.at + pp * SM::LM + 4 * g);
 
     for (int ch = nch - 1; ch >= 0; --ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        __syncthreads();  // previous chunk's tile reads done; R copy written
-        bwd_stage<TI, DK, SM::LK, kBwdThreads>(p.q, bh * N, r0, nrows, C, sm.q, tid, 1);
-        bwd_stage<TI, DK, SM::LK, kBwdThreads>(p.k, bh * N, r0, nrows, C, sm.k, tid, 1);
-        bwd_stage<TI, DV, SM::LV, kBwdThreads>(p.v, bh * N, r0, nrows, C, sm.v, tid, 0);
-        bwd_stage<TI, DV, SM::LV, kBwdThreads>(p.g, bh * N, r0, nrows, C, sm.g, tid, 0);
-        if (tid < 64) {
-            sm.e[tid] = tid < nrows ? p.eps[bh * N + r0 + tid] : 0.f;
-            sm.a[tid] = tid < nrows ? p.inv_den[bh * N + r0 + tid] : 0.f;
+        __syncthreads();  // previous chunk's tile reads done
+        xq.template store<SM::LQ>(sm.q, nrows, tid, true);
+        xk.template store<SM::LK>(sm.k, nrows, tid, true);
+        xv.template store<SM::LV>(sm.v, nrows, tid, false);
+        xg.template store<SM::LG>(sm.g, nrows, tid, false);
+        if (tid < SM::CM) {
+            sm.e[tid] = tid < nrows ? xe : 0.f;
+            sm.a[tid] = tid < nrows ? xa : 0.f;
         }
         __syncthreads();
+        if (ch > 0) fetch(ch - 1);
 
-        const bool has_e = wave < EB, has_c = wave < CB;
-        if (has_e || has_c) {
+        // Over the blocks I >= J, one block per wave and pass (M blocks, then A blocks):
+        //   M_ij = (g_i . v_j + e_i) a_i,  A_ij = (phi(q_i) . phi(k_j)) a_i  (i >= j),
+        // stored transposed, [j][i]; blocks above the diagonal stay zero in LDS.
+        const int nblk = nib * (nib + 1) / 2;
+        for (int b = wave; b < 2 * nblk; b += NW) {
+            const bool is_a = b >= nblk;
+            int I, J;
+            lower_block(is_a ? b - nblk : b, I, J);
+            f32x4 acc = zero4;
+            if (!is_a) {
 #pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                if (J < nib) {
-                    Frag<TC> fvj[NSV], fkj[NSE];
-                    const TC *vrow = &sm.v[(16 * J + pp) * SM::LV];
-                    const TC *krow = &sm.k[(16 * J + pp) * SM::LK];
+                for (int s = 0; s < NSV; ++s) {
+                    Frag<TC> fg, fv;
+                    lds_frag_split_v(fg, gb, 16 * I * SM::LG + 32 * s);
+                    lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
+                    acc = mma(fg, fv, acc);
+                }
+            } else {
 #pragma unroll
-                    for (int s = 0; s < NSV; ++s) lds_frag_split(fvj[s], vrow + 32 * s, vrow + 32 * s + 16, g);
+                for (int s = 0; s < NSE; ++s) {
+                    Frag<TC> fq, fk;
+                    lds_frag_split_v(fq, qb, 16 * I * SM::LQ + 32 * s);
+                    lds_frag_split_v(fk, kb, 16 * J * SM::LK + 32 * s);
+                    acc = mma(fq, fk, acc);
+                }
+            }
+            // lane: queries i = 16 I + 4g + r of token j = 16 J + pp
+            const f32x4 ev = *reinterpret_cast<const f32x4 *>(&sm.e[16 * I + 4 * g]);
+            const f32x4 av = *reinterpret_cast<const f32x4 *>(&sm.a[16 * I + 4 * g]);
 #pragma unroll
-                    for (int s = 0; s < NSE; ++s) lds_frag_split(fkj[s], krow + 32 * s, krow + 32 * s + 16, g);
-                    f32x4 accM[4], accA[4];
+            for (int r = 0; r < 4; ++r) {
+                const bool keep = !(I == J && pp > 4 * g + r);
+                acc[r] = keep ? (is_a ? acc[r] : acc[r] + ev[r]) * av[r] : 0.f;
+            }
+            const int off = (16 * J + pp) * SM::LM + 16 * I + 4 * g;
+            if (!is_a)
+                lds_put4_pair(sm.mh + off, sm.ml + (SM::LO ? off : 0), acc);
+            else
+                lds_put4(sm.at + off, acc);
+        }
+        // R^T rows c' = 16 cb + pp over features (split): A operand of the dv product
+        Frag<TC> frt[NSE];
+        if (has_c) {
 #pragma unroll
-                    for (int I = 0; I < 4; ++I) {
-                        accM[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        accA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (I >= J && I < nib) {
-                            const TC *grow = &sm.g[(16 * I + pp) * SM::LV];
-                            const TC *qrow = &sm.q[(16 * I + pp) * SM::LK];
-                            if (has_e) {
+            for (int s = 0; s < NSE; ++s)
+                lds_frag_tr(frt[s], sm.R, SM::LR, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cb, pp);
+        }
+        __syncthreads();  // M and A blocks are in LDS; R copy reads done
+
+        Frag<TC> fqt[NTS], fgt[NTS];  // phi(Q) (features 16 eb + pp), dO (values 16 cb + pp) over queries
+        if (has_e) {
 #pragma unroll
-                                for (int s = 0; s < NSV; ++s) {
-                                    Frag<TC> fg;
-                                    lds_frag_split(fg, grow + 32 * s, grow + 32 * s + 16, g);
-                                    accM[I] = mma(fg, fvj[s], accM[I]);
-                                }
-                            }
-                            if (has_c) {
+            for (int ip = 0; ip < NTS; ++ip)
+                lds_frag_tr(fqt[ip], sm.q, SM::LQ, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * eb, pp);
+        }
+        if (has_c) {
 #pragma unroll
-                                for (int s = 0; s < NSE; ++s) {
-                                    Frag<TC> fq;
-                                    lds_frag_split(fq, qrow + 32 * s, qrow + 32 * s + 16, g);
-                                    accA[I] = mma(fq, fkj[s], accA[I]);
-                                }
-                            }
+            for (int ip = 0; ip < NTS; ++ip)
+                lds_frag_tr(fgt[ip], sm.g, SM::LG, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * cb, pp);
+        }
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const bool keep = !(I == J && 4 * g + r < pp);  // i >= j
-                                const int i = 16 * I + 4 * g + r;
-                                const float a = sm.a[i];
-                                accM[I][r] = keep ? (accM[I][r] + sm.e[i]) * a : 0.f;
-                                accA[I][r] = keep ? accA[I][r] * a : 0.f;
-                            }
-                        }
-                    }
-                    const int row_local = 16 * J + pp;
-                    const bool valid = row_local < nrows;
-                    const long orow = bh * N + r0 + row_local;
-                    if (has_e) {
-                        Frag<TC> fb[2], fbl[2];  // M as operand value + remainder
+        for (int J = 0; J < NIB; ++J) {
+            if (J < nib) {
+                const int row_local = 16 * J + pp;
+                const bool valid = row_local < nrows;
+                const long orow = bh * N + r0 + row_local;
+                if (has_e) {
+                    // dk(eb, J) = sum_i phi(q_i)(eb) M_ij + R(eb, :) v_j + r(eb), times phi'(k_j)
+                    f32x4 acc = zero4;
 #pragma unroll
-                        for (int ip = 0; ip < 2; ++ip) {
-                            if (2 * ip + 1 >= J) {
-                                acc_to_frag(fb[ip], accM[2 * ip], accM[2 * ip + 1]);
-#pragma unroll
-                                for (int t = 0; t < 4; ++t) {
-                                    fbl[ip].set(t, accM[2 * ip][t] - fb[ip].get(t));
-                                    fbl[ip].set(t + 4, accM[2 * ip + 1][t] - fb[ip].get(t + 4));
-                                }
-                            }
-                        }
-#pragma unroll
-                        for (int es = 0; es < EBW; ++es) {
-                            const int eb = wave + NW * es;
-                            if (eb < EB) {
-                                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                                for (int ip = 0; ip < 2; ++ip) {
-                                    if (2 * ip + 1 >= J && 2 * ip < nib) {
-                                        Frag<TC> fqt;
-                                        lds_frag_tr(fqt, sm.q, SM::LK, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * eb, pp);
-                                        acc = mma(fqt, fb[ip], acc);
-                                        if (sizeof(TC) == 2) acc = mma(fqt, fbl[ip], acc);
-                                    }
-                                }
-#pragma unroll
-                                for (int s = 0; s < NSV; ++s) acc = mma(fragR[es][s], fvj[s], acc);
-                                const TC *kd = &sm.k[row_local * SM::LK + 16 * eb + 4 * g];
-                                f32x4 out;
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    out[r] = (acc[r] + accr[es][r]) * fminf(static_cast<float>(kd[r]), 1.0f);
-                                if (valid) store4<TI>(p.dk, orow * DK + 16 * eb + 4 * g, out);
+                    for (int ip = 0; ip < NTS; ++ip) {
+                        if (2 * ip + 1 >= J) {
+                            Frag<TC> fm;
+                            lds_frag_split_v(fm, mhb, 16 * J * SM::LM + 32 * ip);
+                            acc = mma(fqt[ip], fm, acc);
+                            if constexpr (SM::LO) {
+                                lds_frag_split_v(fm, mlb, 16 * J * SM::LM + 32 * ip);
+                                acc = mma(fqt[ip], fm, acc);
                             }
                         }
                     }
-                    if (has_c) {
-                        Frag<TC> fb[2];
 #pragma unroll
-                        for (int ip = 0; ip < 2; ++ip)
-                            if (2 * ip + 1 >= J) acc_to_frag(fb[ip], accA[2 * ip], accA[2 * ip + 1]);
+                    for (int s = 0; s < NSV; ++s) {
+                        Frag<TC> fv;
+                        lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
+                        acc = mma(fragR[s], fv, acc);
+                    }
+                    const f32x4 kd = lds_get4(kb, 16 * J * SM::LK + 16 * eb);
+                    f32x4 out;
 #pragma unroll
-                        for (int cs = 0; cs < CBW; ++cs) {
-                            const int cb = wave + NW * cs;
-                            if (cb < CB) {
-                                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < 4; ++r) out[r] = (acc[r] + accr[r]) * fminf(kd[r], 1.0f);
+                    if (valid) store4<TI>(p.dk, orow * DK + 16 * eb + 4 * g, out);
+                }
+                if (has_c) {
+                    // dv(cb, J) = sum_i dO_i(cb) A_ij + R^T(cb, :) phi(k_j)
+                    f32x4 acc = zero4;
 #pragma unroll
-                                for (int ip = 0; ip < 2; ++ip) {
-                                    if (2 * ip + 1 >= J && 2 * ip < nib) {
-                                        Frag<TC> fgt;
-                                        lds_frag_tr(fgt, sm.g, SM::LV, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * cb, pp);
-                                        acc = mma(fgt, fb[ip], acc);
-                                    }
-                                }
-#pragma unroll
-                                for (int s = 0; s < NSE; ++s) {
-                                    Frag<TC> frt;  // R^T rows c', split over features
-                                    lds_frag_tr(frt, sm.R, SM::LR, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cb, pp);
-                                    acc = mma(frt, fkj[s], acc);
-                                }
-                                if (valid) store4<TI>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
-                            }
+                    for (int ip = 0; ip < NTS; ++ip) {
+                        if (2 * ip + 1 >= J) {
+                            Frag<TC> fa;
+                            lds_frag_split_v(fa, atb, 16 * J * SM::LM + 32 * ip);
+                            acc = mma(fgt[ip], fa, acc);
                         }
                     }
+#pragma unroll
+                    for (int s = 0; s < NSE; ++s) {
+                        Frag<TC> fk;
+                        lds_frag_split_v(fk, kb, 16 * J * SM::LK + 32 * s);
+                        acc = mma(frt[s], fk, acc);
+                    }
+                    if (valid) store4<TI>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
                 }
             }
         }
-        __syncthreads();  // every wave is done reading the R copy
         if (has_e) {
-            // state carry: R^T(c', eb) += g^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
+            // state carry: R^T(c', eb) += dO^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+            for (int s = 0; s < NTS; ++s) {
                 if (s < nts) {
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sm.a[32 * s + 4 * g]);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sm.a[32 * s + 16 + 4 * g]);
+                    const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.e[32 * s + 4 * g]);
+                    const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sm.e[32 * s + 16 + 4 * g]);
                     // e as a pair of operands (value and rounding remainder) so that
                     // r keeps fp32-level accuracy with bf16 operands
-                    Frag<TC> fq[EBW], fe, fe_lo;
+                    Frag<TC> fq, fe, fe_lo;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float e = sm.e[32 * s + 8 * g + t];
-                        fe.set(t, e);
-                        fe_lo.set(t, e - fe.get(t));
+                    for (int t = 0; t < 4; ++t) {
+                        fq.set(t, fqt[s].get(t) * a0[t]);
+                        fq.set(t + 4, fqt[s].get(t + 4) * a1[t]);
+                        fe.set(t, e0[t]);
+                        fe.set(t + 4, e1[t]);
+                        fe_lo.set(t, e0[t] - fe.get(t));
+                        fe_lo.set(t + 4, e1[t] - fe.get(t + 4));
                     }
-#pragma unroll
-                    for (int es = 0; es < EBW; ++es) {
-                        const int eb = wave + NW * es;
-                        if (eb < EB) {
-                            lds_frag_tr(fq[es], sm.q, SM::LK, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * eb, pp);
-#pragma unroll
-                            for (int t = 0; t < 8; ++t)  // slot t holds token 32s + 8g + t
-                                fq[es].set(t, fq[es].get(t) * sm.a[32 * s + 8 * g + t]);
-                            accr[es] = mma(fq[es], fe, accr[es]);
-                            if (sizeof(TC) == 2) accr[es] = mma(fq[es], fe_lo, accr[es]);
-                        }
-                    }
+                    accr = mma(fq, fe, accr);
+                    if constexpr (SM::LO) accr = mma(fq, fe_lo, accr);
 #pragma unroll
                     for (int cv = 0; cv < CV; ++cv) {
-                        Frag<TC> fgt;
-                        lds_frag_tr(fgt, sm.g, SM::LV, 32 * s + 8 * g, 32 * s + 8 * g + 4, 16 * cv, pp);
-#pragma unroll
-                        for (int es = 0; es < EBW; ++es)
-                            if (wave + NW * es < EB) accR[cv][es] = mma(fgt, fq[es], accR[cv][es]);
+                        Frag<TC> fgc;
+                        lds_frag_tr(fgc, sm.g, SM::LG, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
+                        accR[cv] = mma(fgc, fq, accR[cv]);
                     }
                 }
             }
-            refresh();
+            refresh();  // the R copy's readers of this chunk passed the barrier above
         }
     }
 }

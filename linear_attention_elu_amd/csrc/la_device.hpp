@@ -194,6 +194,67 @@ __device__ __forceinline__ void lds_frag_split_at(Frag<TC> &f, lds_cptr<TC> lo, 
     }
 }
 
+// Volatile LDS accesses: each stays a separate ds_read_b64 / ds_write_b64 with
+// an immediate offset from one base register (the compiler does not pair
+// volatile accesses into ds_read2 / ds_write2).
+template <typename T> using lds_vptr = const volatile T __attribute__((address_space(3))) *;
+template <typename T> using lds_wptr = volatile T __attribute__((address_space(3))) *;
+
+template <typename T> __device__ __forceinline__ lds_vptr<T> lds_v(const T *p) {
+    return (lds_vptr<T>)(lds_cptr<T>)p;
+}
+template <typename T> __device__ __forceinline__ lds_wptr<T> lds_w(T *p) {
+    return (lds_wptr<T>)(T __attribute__((address_space(3))) *)p;
+}
+
+// Four consecutive elements at base[off] as floats.
+__device__ __forceinline__ f32x4 lds_get4(lds_vptr<__bf16> base, int off) {
+    const bf16x4 b = *reinterpret_cast<lds_vptr<bf16x4>>(base + off);
+    return __builtin_convertvector(b, f32x4);
+}
+__device__ __forceinline__ f32x4 lds_get4(lds_vptr<float> base, int off) {
+    return *reinterpret_cast<lds_vptr<f32x4>>(base + off);
+}
+
+// Split-assignment fragment: slots 0..3 from base[off..], slots 4..7 from
+// base[off + 16..] (base = the lane's address of row p, column 4g).
+__device__ __forceinline__ void lds_frag_split_v(Frag<__bf16> &f, lds_vptr<__bf16> base, int off) {
+    const bf16x4 a = *reinterpret_cast<lds_vptr<bf16x4>>(base + off);
+    const bf16x4 b = *reinterpret_cast<lds_vptr<bf16x4>>(base + off + 16);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+__device__ __forceinline__ void lds_frag_split_v(Frag<float> &f, lds_vptr<float> base, int off) {
+    const f32x4 a = *reinterpret_cast<lds_vptr<f32x4>>(base + off);
+    const f32x4 b = *reinterpret_cast<lds_vptr<f32x4>>(base + off + 16);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.v[t] = a[t];
+        f.v[t + 4] = b[t];
+    }
+}
+
+// Four floats stored as four elements of the tile type at p[0..3].
+__device__ __forceinline__ void lds_put4(__bf16 *p, const f32x4 &x) {
+    *reinterpret_cast<lds_wptr<bf16x4>>(lds_w(p)) = __builtin_convertvector(x, bf16x4);
+}
+__device__ __forceinline__ void lds_put4(float *p, const f32x4 &x) {
+    *reinterpret_cast<lds_wptr<f32x4>>(lds_w(p)) = x;
+}
+
+// Four floats as an operand value (hi) and, for bf16, the bf16 rounding of
+// what that value leaves out (lo): hi + lo carries about 16 significant bits.
+__device__ __forceinline__ void lds_put4_pair(__bf16 *hi, __bf16 *lo, const f32x4 &x) {
+    const bf16x4 h = __builtin_convertvector(x, bf16x4);
+    const f32x4 r = x - __builtin_convertvector(h, f32x4);
+    *reinterpret_cast<lds_wptr<bf16x4>>(lds_w(hi)) = h;
+    *reinterpret_cast<lds_wptr<bf16x4>>(lds_w(lo)) = __builtin_convertvector(r, bf16x4);
+}
+__device__ __forceinline__ void lds_put4_pair(float *hi, float *, const f32x4 &x) { lds_put4(hi, x); }
+
 // Transposed reads of a row-major tile (LDS), for operands whose K index is
 // the tile's row index.  The result slots t = 0..3 of the lane at position p
 // are tile[row0 + t][col0 + p] and slots 4..7 are tile[row1 + t][col0 + p];
