@@ -111,8 +111,9 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
     }
 
     // Rows [0, CM) of the tile (leading dimension LD): phi of the loaded
-    // values (with_phi) or the values themselves; zero past nrows.
-    template <int LD>
+    // values (with_phi) or the values themselves; zero past nrows (FULL: the
+    // caller knows nrows == CM).
+    template <int LD, bool FULL>
     __device__ __forceinline__ void store(TI *tile, int nrows, int tid, bool with_phi) const {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -121,7 +122,7 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
             uint4 w = make_uint4(0, 0, 0, 0);
-            if (row < nrows) {
+            if (FULL || row < nrows) {
                 if (!with_phi) {
                     w = u[it];
                 } else {
@@ -250,10 +251,17 @@ la_bwd_dq_kernel(const BwdParams p) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
         __syncthreads();  // previous chunk's tile reads done
-        xk.template store<SM::LK>(sm.k, nrows, tid, true);
-        xq.template store<SM::LQ>(sm.q, nrows, tid, true);
-        xv.template store<SM::LV>(sm.v, nrows, tid, false);
-        xg.template store<SM::LG>(sm.g, nrows, tid, false);
+        if (nrows == SM::CM) {
+            xk.template store<SM::LK, true>(sm.k, nrows, tid, true);
+            xq.template store<SM::LQ, true>(sm.q, nrows, tid, true);
+            xv.template store<SM::LV, true>(sm.v, nrows, tid, false);
+            xg.template store<SM::LG, true>(sm.g, nrows, tid, false);
+        } else {
+            xk.template store<SM::LK, false>(sm.k, nrows, tid, true);
+            xq.template store<SM::LQ, false>(sm.q, nrows, tid, true);
+            xv.template store<SM::LV, false>(sm.v, nrows, tid, false);
+            xg.template store<SM::LG, false>(sm.g, nrows, tid, false);
+        }
         __syncthreads();
         if (ch + 1 < nch) fetch(ch + 1);
 
@@ -324,8 +332,8 @@ la_bwd_dq_kernel(const BwdParams p) {
                         px += fq[r] * ax[r];
                         pz += fq[r] * az[r];
                     }
-                    px = sum_over_groups(px);
-                    pz = sum_over_groups(pz);
+                    px = sum_over_groups_swap(px);
+                    pz = sum_over_groups_swap(pz);
                     if (g == 0) {
                         sm.red[wave][16 * I + pp][0] = px;
                         sm.red[wave][16 * I + pp][1] = pz;
@@ -495,10 +503,17 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
         __syncthreads();  // previous chunk's tile reads done
-        xq.template store<SM::LQ>(sm.q, nrows, tid, true);
-        xk.template store<SM::LK>(sm.k, nrows, tid, true);
-        xv.template store<SM::LV>(sm.v, nrows, tid, false);
-        xg.template store<SM::LG>(sm.g, nrows, tid, false);
+        if (nrows == SM::CM) {
+            xq.template store<SM::LQ, true>(sm.q, nrows, tid, true);
+            xk.template store<SM::LK, true>(sm.k, nrows, tid, true);
+            xv.template store<SM::LV, true>(sm.v, nrows, tid, false);
+            xg.template store<SM::LG, true>(sm.g, nrows, tid, false);
+        } else {
+            xq.template store<SM::LQ, false>(sm.q, nrows, tid, true);
+            xk.template store<SM::LK, false>(sm.k, nrows, tid, true);
+            xv.template store<SM::LV, false>(sm.v, nrows, tid, false);
+            xg.template store<SM::LG, false>(sm.g, nrows, tid, false);
+        }
         if (tid < SM::CM) {
             sm.e[tid] = tid < nrows ? xe : 0.f;
             sm.a[tid] = tid < nrows ? xa : 0.f;

@@ -352,4 +352,15 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return x;
 }
 
+// The same sum with the gfx950 lane swaps (VALU, no LDS round trip): the
+// 16-lane swap pairs rows 0-1 and 2-3 of the wave, the 32-lane swap its halves.
+__device__ __forceinline__ float sum_over_groups_swap(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace la
