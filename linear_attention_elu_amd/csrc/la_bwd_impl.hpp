@@ -110,35 +110,35 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
         }
     }
 
-    // Rows [0, CM) of the tile (leading dimension LD): phi of the loaded
-    // values (with_phi) or the values themselves; zero past nrows (FULL: the
-    // caller knows nrows == CM).
+    // phi of the loaded values, in place (16-byte vectors of TI).
+    __device__ __forceinline__ void apply_phi() {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            float x[VEC];
+            unpack16(u[it], x, TI());
+            if constexpr (sizeof(TI) == 2) {
+                const f32x4 a = {phi(x[0]), phi(x[1]), phi(x[2]), phi(x[3])};
+                const f32x4 b = {phi(x[4]), phi(x[5]), phi(x[6]), phi(x[7])};
+                const uint2 pa = pack_bf16x4(a), pb = pack_bf16x4(b);
+                u[it] = make_uint4(pa.x, pa.y, pb.x, pb.y);
+            } else {
+                u[it] = make_uint4(__float_as_uint(phi(x[0])), __float_as_uint(phi(x[1])),
+                                   __float_as_uint(phi(x[2])), __float_as_uint(phi(x[3])));
+            }
+        }
+    }
+
+    // Rows [0, CM) of the tile (leading dimension LD) from the registers; zero
+    // past nrows (FULL: the caller knows nrows == CM).
     template <int LD, bool FULL>
-    __device__ __forceinline__ void store(TI *tile, int nrows, int tid, bool with_phi) const {
+    __device__ __forceinline__ void store(TI *tile, int nrows, int tid) const {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int idx = tid + it * NT;
             if (NV % NT != 0 && idx >= NV) continue;
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (FULL || row < nrows) {
-                if (!with_phi) {
-                    w = u[it];
-                } else {
-                    float x[VEC];
-                    unpack16(u[it], x, TI());
-                    if constexpr (sizeof(TI) == 2) {
-                        const f32x4 a = {phi(x[0]), phi(x[1]), phi(x[2]), phi(x[3])};
-                        const f32x4 b = {phi(x[4]), phi(x[5]), phi(x[6]), phi(x[7])};
-                        const uint2 pa = pack_bf16x4(a), pb = pack_bf16x4(b);
-                        w = make_uint4(pa.x, pa.y, pb.x, pb.y);
-                    } else {
-                        w = make_uint4(__float_as_uint(phi(x[0])), __float_as_uint(phi(x[1])),
-                                       __float_as_uint(phi(x[2])), __float_as_uint(phi(x[3])));
-                    }
-                }
-            }
+            const uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
         }
     }
@@ -194,8 +194,8 @@ la_bwd_dq_kernel(const BwdParams p) {
     const int row_begin = seg * p.L;
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + C - 1) / C;
-    const int nib = C / 16, nts = (C + 31) / 32;
-    const bool active = wave < EB;
+    const int nib = C / 16;
+    const bool active = EB >= NW || wave < EB;
     const int eb = wave;
 
     {
@@ -238,7 +238,11 @@ la_bwd_dq_kernel(const BwdParams p) {
         xv.load(p.v, bh * N, r0, nrows, tid);
         xg.load(p.g, bh * N, r0, nrows, tid);
     };
-    if (nch > 0) fetch(0);
+    if (nch > 0) {
+        fetch(0);
+        xk.apply_phi();
+        xq.apply_phi();
+    }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
     const lds_vptr<TC> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
@@ -251,16 +255,17 @@ la_bwd_dq_kernel(const BwdParams p) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
         __syncthreads();  // previous chunk's tile reads done
+        // (phi(k), phi(q) were applied in registers during the previous chunk)
         if (nrows == SM::CM) {
-            xk.template store<SM::LK, true>(sm.k, nrows, tid, true);
-            xq.template store<SM::LQ, true>(sm.q, nrows, tid, true);
-            xv.template store<SM::LV, true>(sm.v, nrows, tid, false);
-            xg.template store<SM::LG, true>(sm.g, nrows, tid, false);
+            xk.template store<SM::LK, true>(sm.k, nrows, tid);
+            xq.template store<SM::LQ, true>(sm.q, nrows, tid);
+            xv.template store<SM::LV, true>(sm.v, nrows, tid);
+            xg.template store<SM::LG, true>(sm.g, nrows, tid);
         } else {
-            xk.template store<SM::LK, false>(sm.k, nrows, tid, true);
-            xq.template store<SM::LQ, false>(sm.q, nrows, tid, true);
-            xv.template store<SM::LV, false>(sm.v, nrows, tid, false);
-            xg.template store<SM::LG, false>(sm.g, nrows, tid, false);
+            xk.template store<SM::LK, false>(sm.k, nrows, tid);
+            xq.template store<SM::LQ, false>(sm.q, nrows, tid);
+            xv.template store<SM::LV, false>(sm.v, nrows, tid);
+            xg.template store<SM::LG, false>(sm.g, nrows, tid);
         }
         __syncthreads();
         if (ch + 1 < nch) fetch(ch + 1);
@@ -355,7 +360,7 @@ la_bwd_dq_kernel(const BwdParams p) {
                         t += sm.red[w][row_local][0];
                         den += sm.red[w][row_local][1];
                     }
-                    const float inv = 1.0f / den;
+                    const float inv = __builtin_amdgcn_rcpf(den);
                     const float coef = t * inv;
                     const bool valid = row_local < nrows;
                     const long orow = bh * N + r0 + row_local;
@@ -371,17 +376,21 @@ la_bwd_dq_kernel(const BwdParams p) {
                     if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
                 }
             }
+        }
+        // phi of the next chunk's rows (after the last chunk the registers are not used again)
+        xk.apply_phi();
+        xq.apply_phi();
+        if (active) {
             // state carry: S^T(c', eb) += V^T(c') phi(K)(eb), z(eb) += phi(K)(eb)^T 1
+            // (token rows past the chunk are zero in the tiles)
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
-                if (s < nts) {
-                    accZ = mma(fkt[s], ones, accZ);
+                accZ = mma(fkt[s], ones, accZ);
 #pragma unroll
-                    for (int cv = 0; cv < CV; ++cv) {
-                        Frag<TC> fvt;
-                        lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
-                        accS[cv] = mma(fvt, fkt[s], accS[cv]);
-                    }
+                for (int cv = 0; cv < CV; ++cv) {
+                    Frag<TC> fvt;
+                    lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
+                    accS[cv] = mma(fvt, fkt[s], accS[cv]);
                 }
             }
             refresh();
@@ -435,8 +444,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     const int row_begin = seg * p.L;
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + C - 1) / C;
-    const int nib = C / 16, nts = (C + 31) / 32;
-    const bool has_e = wave < EB, has_c = wave < CB;
+    const int nib = C / 16;
+    const bool has_e = EB >= NW || wave < EB, has_c = CB >= NW || wave < CB;
     const int eb = wave, cb = wave;
 
     {
@@ -488,7 +497,11 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             xa = p.inv_den[t];
         }
     };
-    if (nch > 0) fetch(nch - 1);
+    if (nch > 0) {
+        fetch(nch - 1);
+        xq.apply_phi();
+        xk.apply_phi();
+    }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
     const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 4 * g);
@@ -503,16 +516,17 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
         __syncthreads();  // previous chunk's tile reads done
+        // (phi(q), phi(k) were applied in registers during the previous chunk)
         if (nrows == SM::CM) {
-            xq.template store<SM::LQ, true>(sm.q, nrows, tid, true);
-            xk.template store<SM::LK, true>(sm.k, nrows, tid, true);
-            xv.template store<SM::LV, true>(sm.v, nrows, tid, false);
-            xg.template store<SM::LG, true>(sm.g, nrows, tid, false);
+            xq.template store<SM::LQ, true>(sm.q, nrows, tid);
+            xk.template store<SM::LK, true>(sm.k, nrows, tid);
+            xv.template store<SM::LV, true>(sm.v, nrows, tid);
+            xg.template store<SM::LG, true>(sm.g, nrows, tid);
         } else {
-            xq.template store<SM::LQ, false>(sm.q, nrows, tid, true);
-            xk.template store<SM::LK, false>(sm.k, nrows, tid, true);
-            xv.template store<SM::LV, false>(sm.v, nrows, tid, false);
-            xg.template store<SM::LG, false>(sm.g, nrows, tid, false);
+            xq.template store<SM::LQ, false>(sm.q, nrows, tid);
+            xk.template store<SM::LK, false>(sm.k, nrows, tid);
+            xv.template store<SM::LV, false>(sm.v, nrows, tid);
+            xg.template store<SM::LG, false>(sm.g, nrows, tid);
         }
         if (tid < SM::CM) {
             sm.e[tid] = tid < nrows ? xe : 0.f;
@@ -635,11 +649,15 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                 }
             }
         }
+        // phi of the previous chunk's rows (after the first chunk the registers are not used again)
+        xq.apply_phi();
+        xk.apply_phi();
         if (has_e) {
             // state carry: R^T(c', eb) += dO^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
+            // (a = 0 for token rows past the chunk)
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
-                if (s < nts) {
+                {
                     const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sm.a[32 * s + 4 * g]);
                     const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sm.a[32 * s + 16 + 4 * g]);
                     const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sm.e[32 * s + 4 * g]);
