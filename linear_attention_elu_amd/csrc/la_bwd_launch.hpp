@@ -87,12 +87,16 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     a.state_P = Pf;
     a.state_mult = 1;
     if (Pq > 1) {
+        // prefix sums: the last dq segment's own fine segments are not needed
+        const int nagg = (Pq - 1) * mult_q;
         a.k = d.k;
         a.v = d.v;
         a.seg_out = pre;
-        agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+        a.seg_base = 0;
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
+        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream)) != hipSuccess)
+            return err;
     }
 
     BwdParams b{};
@@ -121,9 +125,13 @@ hipError_t run_bwd_t(const BwdDesc &d) {
         a.kscale = inv_den;
         a.zw = eps;
         a.seg_out = suf;
-        aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+        // suffix sums: the first dk/dv segment's own fine segments are not needed
+        const int first = mult_kv;
+        a.seg_base = first;
+        aggw_kernel<<<dim3((unsigned)BH, (unsigned)(Pf - first)), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, d.stream)) != hipSuccess) return err;
+        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, first, d.stream)) != hipSuccess)
+            return err;
     }
     b.state = Pkv > 1 ? suf : nullptr;
     b.state_mult = mult_kv;

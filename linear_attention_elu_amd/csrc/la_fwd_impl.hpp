@@ -84,6 +84,7 @@ struct FwdParams {
     int L;                  // tokens per segment of this launch (a multiple of the chunk size)
     int state_P;            // segments per (bh) in the state array
     int state_mult;         // segment s of this launch starts at state slot s * state_mult
+    int seg_base;           // segment of workgroup row blockIdx.y: seg_base + blockIdx.y
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -164,7 +165,7 @@ la_chunk_kernel(const FwdParams p) {
     const int g = lane >> 4;
     const int pp = lane & 15;
     const long bh = blockIdx.x;
-    const int seg = blockIdx.y;
+    const int seg = p.seg_base + (int)blockIdx.y;
     const int N = p.N;
     const int row_begin = seg * p.L;
     const int row_end = min(N, row_begin + p.L);
@@ -743,7 +744,7 @@ la_chunk_kernel(const FwdParams p) {
     if (AGGM) {
         Sdst = p.seg_out + (bh * p.state_P + seg) * (long)(DK * DV + DK);
         zdst = Sdst + DK * DV;
-    } else if (MODE == MODE_CAUSAL && seg == (int)gridDim.y - 1 && p.S_fin) {
+    } else if (MODE == MODE_CAUSAL && blockIdx.y == gridDim.y - 1 && p.S_fin) {
         Sdst = p.S_fin + bh * (long)(DK * DV);
         zdst = p.z_fin + bh * (long)DK;
     }

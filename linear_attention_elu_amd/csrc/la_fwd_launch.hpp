@@ -49,12 +49,16 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
         p.S_fin = d.S_out;
         p.z_fin = d.z_out;
         if (Pm > 1) {
+            // Only the segments before the last one need their sums: the
+            // last causal segment starts at fine slot (Pm - 1) * mult.
+            const int nagg = (Pm - 1) * mult;
             p.seg_out = d.ws;
             p.L = Lf;
             p.state_mult = 1;
-            agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+            agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
-            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, d.stream)) != hipSuccess) return err;
+            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, nagg, d.stream)) != hipSuccess)
+                return err;
             p.seg_state = d.ws;
             p.state_mult = mult;
             p.L = Lf * mult;
@@ -74,7 +78,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (Pf > 1) {
-        if ((err = launch_seg_scan(d.ws, nullptr, nullptr, BH, Pf, DK, DV, 1, d.stream)) != hipSuccess) return err;
+        if ((err = launch_seg_scan(d.ws, nullptr, nullptr, BH, Pf, DK, DV, 1, Pf, d.stream)) != hipSuccess) return err;
     }
     // The read-out is independent per row: split it on its own.
     int La = 0;

@@ -62,11 +62,13 @@ long resident_workgroups(const void *kernel, OccCache &cache, int threads = 256)
 inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 
 // Per-(bh, element) pass over the P segment states stored at ws[bh][P][DK*DV + DK]:
-// mode 0 replaces them by their exclusive prefix (S0, z0 folded in when given),
-// mode 1 writes their total into segment slot 0, mode 2 replaces them by their
-// exclusive suffix.  Fixed summation order.
+// mode 0 replaces slots [0, lim) by their exclusive prefix (S0, z0 folded in
+// when given) and writes the sum of all of them into slot lim (when lim < P);
+// mode 1 writes the total of all P slots into slot 0; mode 2 replaces slots
+// [lim, P) by their exclusive suffix and writes the sum of all of them into
+// slot lim - 1 (when lim > 0).  Other slots are not touched.  Fixed order.
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
-                           int mode, hipStream_t stream);
+                           int mode, int lim, hipStream_t stream);
 
 hipError_t run_fwd_dk16(const FwdDesc &d, bool causal);
 hipError_t run_fwd_dk32(const FwdDesc &d, bool causal);

@@ -11,11 +11,17 @@
 
 namespace la {
 
-// Pass over segments, per (bh, element): exclusive prefix (mode 0, the
-// initial state folded in), total into slot 0 (mode 1) or exclusive suffix
-// (mode 2).  Fixed order.
+// Pass over segments, per (bh, element), in a fixed order:
+//   mode 0: exclusive prefix, the initial state folded in.  Only slots
+//           [0, lim) hold aggregates; slots [0, lim] are written (slot lim,
+//           when it exists, receives the sum of all of them).
+//   mode 1: total of all P slots into slot 0 (lim unused).
+//   mode 2: exclusive suffix.  Only slots [lim, P) hold aggregates; slots
+//           [max(lim - 1, 0), P) are written.
+// Slots outside those ranges are neither read nor written, so a caller
+// aggregates only the segments whose sums some later pass reads.
 static __global__ void __launch_bounds__(256)
-la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode) {
+la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode, int lim) {
     const int SS = DK * DV + DK;
     const long bh = blockIdx.x;
     const int idx = blockIdx.y * 256 + threadIdx.x;
@@ -28,30 +34,33 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
         } else if (z0) {
             run = z0[bh * (long)DK + (idx - DK * DV)];
         }
-        for (int s = 0; s < P; ++s) {
+        for (int s = 0; s < lim; ++s) {
             const float a = base[(long)s * SS];
             base[(long)s * SS] = run;
             run += a;
         }
+        if (lim < P) base[(long)lim * SS] = run;
     } else if (mode == 1) {
         float run = 0.f;
         for (int s = 0; s < P; ++s) run += base[(long)s * SS];
         base[0] = run;
     } else {
         float run = 0.f;  // exclusive suffix: the sum over the later segments
-        for (int s = P - 1; s >= 0; --s) {
+        for (int s = P - 1; s >= lim; --s) {
             const float a = base[(long)s * SS];
             base[(long)s * SS] = run;
             run += a;
         }
+        if (lim > 0) base[(long)(lim - 1) * SS] = run;
     }
 }
 
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
-                           int mode, hipStream_t stream) {
+                           int mode, int lim, hipStream_t stream) {
+    if (lim < 0 || lim > P) return hipErrorInvalidValue;
     const long SS = state_floats(DK, DV);
     const dim3 grid((unsigned)BH, (unsigned)((SS + 255) / 256));
-    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode);
+    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode, lim);
     return hipGetLastError();
 }
 
