@@ -47,6 +47,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "la_device.hpp"
 
@@ -123,6 +124,15 @@ template <int DK, int DV, typename TI, int CT, int MODE> constexpr int fwd_waves
 
 #define LA_INLINE __attribute__((always_inline))
 
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}).
+template <typename F, int... Is>
+__device__ LA_INLINE void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // OBF: the output o is bf16 (else fp32).
 template <int DK, int DV, typename TI, int MODE, int CT, bool OBF>
 __global__ void __launch_bounds__((fwd_threads<DK, DV, TI>()))
@@ -133,6 +143,14 @@ la_chunk_kernel(const FwdParams p) {
     constexpr bool SPLIT = fwd_split<DK, DV, TI>();
     constexpr int kThreads = fwd_threads<DK, DV, TI>();
     constexpr int NBUF = T::NBUF;
+    // Register sets of the staging waves, i.e. chunks loaded ahead.  The
+    // causal chunk loop runs one workgroup per CU and its staging waves have
+    // registers to spare under the compute waves' allocation: four sets keep
+    // about 96 KB of loads in flight per CU (two sets measured about 2%
+    // slower).  The aggregate and read-out passes, two workgroups per CU,
+    // keep two.  A power of two, and even where NBUF = 2.
+    constexpr int NSET = (SPLIT && MODE == MODE_CAUSAL) ? 4 : 2;
+    static_assert(NSET == 2 || NSET == 4 || NSET == 8, "register sets: 2, 4 or 8");
     constexpr int VEC = Store<TI>::VEC;
     constexpr int NE = DK / 16;            // feature tiles
     constexpr int NSE = (DK + 31) / 32;    // feature K steps
@@ -197,10 +215,10 @@ la_chunk_kernel(const FwdParams p) {
         auto q_on = [&](int i) { return (CT * VQ) % kRoleThreads == 0 || rq0 + i * RSQ < CT; };
         auto v_on = [&](int i) { return (CT * VV) % kRoleThreads == 0 || rv0 + i * RSV < CT; };
 
-        // Two register sets; chunk j lives in set j & 1.
-        uint4 rq[2][NEED_Q ? NLQ : 1], rk[2][NEED_K ? NLQ : 1], rv[2][NEED_K ? NLV : 1];
-        float rw[2] = {0.f, 0.f};
-        float rks[2][NKS];
+        // NSET register sets; chunk j lives in set j % NSET.
+        uint4 rq[NSET][NEED_Q ? NLQ : 1], rk[NSET][NEED_K ? NLQ : 1], rv[NSET][NEED_K ? NLV : 1];
+        float rw[NSET] = {};
+        float rks[NSET][NKS];
 
         // Load chunk c into set S.  FULL: all rows valid (uniform base, fixed
         // lane offsets); otherwise row indices are clamped to the segment.
@@ -316,46 +334,49 @@ la_chunk_kernel(const FwdParams p) {
             }
         };
         // One step of the split layout's general loop at chunk j: stage chunk
-        // j from its register set, then refill that set with chunk j + 2.
+        // j from its register set, then refill that set with chunk j + NSET.
         auto step_split = [&](auto set_tag, int j) LA_INLINE {
             const int b = NBUF == 2 ? (j & 1) : 0;
             if (j < nfull) stage(set_tag, Full{}, b, CT);
             else stage(set_tag, Part{}, b, rows_of(j));
-            if (j + 2 < nch) load_any(set_tag, j + 2);
+            if (j + NSET < nch) load_any(set_tag, j + NSET);
+        };
+        auto step_split_any = [&](int j) LA_INLINE {  // j >= 0
+            static_for<NSET>([&](auto u) LA_INLINE {
+                if ((j & (NSET - 1)) == decltype(u)::value) step_split(u, j);
+            });
         };
 
     if constexpr (SPLIT) {
       if (stager) {
         // ================= staging waves: their whole loop =================
-        // Step j stages chunk j (register set j & 1) into buffer j & 1 and
-        // refills that set with chunk j + 2, then meets the compute waves at
-        // a barrier.  The loop starts at j = -2 with loads only, so every load
-        // of the steady state is issued by the same instructions and the wait
-        // before staging a set covers that set's loads, not the other's.
+        // Step j stages chunk j (register set j % NSET) into buffer j & 1 and
+        // refills that set with chunk j + NSET, then meets the compute waves
+        // at a barrier.  The loop starts at j = -NSET with loads only, so
+        // every load of the steady state is issued by the same instructions
+        // and the wait before staging a set covers that set's loads, not the
+        // later sets'.
         __syncthreads();  // the zero fill is complete before any tile write
-        int j = -2;
+        int j = -NSET;
         if constexpr (NBUF == 2) {
-            // (the first trip, j = -2 < nfull - 1, always runs: it loads chunks 0 and 1)
-            for (; j + 1 < nfull; j += 2) {  // chunks j, j + 1 are full
-                if (j >= 0) stage(S0t{}, Full{}, 0, CT);
-                load_any(S0t{}, j + 2);
-                if (j >= 0) __syncthreads();
-                if (j >= 0) stage(S1t{}, Full{}, 1, CT);
-                load_any(S1t{}, j + 3);
-                if (j >= 0) __syncthreads();
+            // (the first trip, j = -NSET, always runs: it loads chunks 0 .. NSET - 1)
+            for (; j + NSET - 1 < nfull; j += NSET) {  // chunks j .. j + NSET - 1 are full
+                static_for<NSET>([&](auto u) LA_INLINE {
+                    constexpr int U = decltype(u)::value;
+                    if (j >= 0) stage(u, Full{}, U & 1, CT);
+                    load_any(u, j + U + NSET);
+                    if (j >= 0) __syncthreads();
+                });
             }
             for (; j < nch; ++j) {
-                if (j & 1) step_split(S1t{}, j);
-                else step_split(S0t{}, j);
+                step_split_any(j);
                 __syncthreads();
             }
         } else {
-            load_any(S0t{}, 0);
-            load_any(S1t{}, 1);
+            static_for<NSET>([&](auto u) LA_INLINE { load_any(u, decltype(u)::value); });
             for (j = 0; j < nch; ++j) {
                 if (j > 0) __syncthreads();  // the compute waves are done with the buffer
-                if (j & 1) step_split(S1t{}, j);
-                else step_split(S0t{}, j);
+                step_split_any(j);
                 __syncthreads();
             }
         }
