@@ -165,13 +165,46 @@ def bench_decode(dev, T=3072, B=256, H=8, d=32, seed=0, reps=5):
     steps_per_s = T / (ms * 1e-3)
     per_step_bytes = B * H * (2 * d * d * 4 + 2 * d * 4 + 3 * d * 4 + d * 4)
     gbs = per_step_bytes * steps_per_s / 1e9
+    floor_us = graph_node_floor_us(dev, T, reps)
+    # a step can take no less than the node floor plus its bytes at the HBM peak
+    ceiling = per_step_bytes / (floor_us * 1e-6 + per_step_bytes / (HBM_PEAK_GBS * 1e9)) / 1e9 / HBM_PEAK_GBS
     return {
         "workload": f"decode_fp32_T{T}_B{B}_H{H}_d{d}", "steps": T, "ms_total": round(ms, 4),
         "us_per_step": round(ms * 1e3 / T, 4), "steps_per_s": round(steps_per_s, 1),
         "tokens_per_s": round(steps_per_s * B, 1), "bytes_per_step": per_step_bytes,
         "achieved_GBs": round(gbs, 1), "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "timing": "one HIP graph of all steps, median of %d replays, launch gaps included" % reps,
+        "graph_node_floor_us": round(floor_us, 3), "hbm_frac_ceiling_one_launch_per_step": round(ceiling, 4),
     }
+
+
+def graph_node_floor_us(dev, T, reps):
+    """Time per node of a HIP graph of T one-element fills: what one kernel launch
+    per decode step costs before the kernel does any work."""
+    import torch
+
+    x = torch.zeros(1, device=dev)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        x.fill_(1.0)
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(T):
+                x.fill_(1.0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for r in range(reps + 1):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            times.append(start.elapsed_time(stop))
+    return statistics.median(times) * 1e3 / T
 
 
 def bench_noncausal(dev, steps=100, warmup=20, B=4, H=8, N=4096, d=64, seed=0):

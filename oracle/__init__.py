@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     fwd_noncausal,
     decode_step,
     bwd_causal,
+    bwd_noncausal,
     num_threads,
     library_path,
     load_variant,

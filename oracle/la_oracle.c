@@ -284,3 +284,81 @@ void oracle_bwd_causal_f64(const double *q, const double *k, const double *v,
         free(Sp);
     }
 }
+
+/*
+ * Gradient of the non-causal form (blog digest "Method / key components 2)";
+ * velog review sections 3.2 and 3.5).  The pages give no formula; this is the
+ * exact gradient of out_i = num_i / den_i with num_i = phi(q_i)^T S and
+ * den_i = phi(q_i) . z, S and z summed over all N tokens.  With the same
+ * augmented vectors as the causal gradient, V'_j = [v_j, 1] and
+ * G'_i = [g_i / den_i, -(g_i . out_i) / den_i]:
+ *   S' = sum_j phi(k_j) V'_j^T,   dL/dphi(q_i) = S' G'_i
+ *   R' = sum_i phi(q_i) G'_i^T,   dL/dphi(k_j) = R' V'_j,  dL/dv_j = R^T phi(k_j)
+ * (R = the first dv columns of R'), then dq = dL/dphi(q) * phi'(q) and
+ * dk = dL/dphi(k) * phi'(k).  The sums are full sums, not running ones.
+ */
+void oracle_bwd_noncausal_f64(const double *q, const double *k, const double *v,
+                              const double *g, double *dq, double *dk_out, double *dv_out,
+                              int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int dv1 = dv + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *qb = q + bh * (long)N * dk;
+        const double *kb = k + bh * (long)N * dk;
+        const double *vb = v + bh * (long)N * dv;
+        const double *gb = g + bh * (long)N * dv;
+        double *dqb = dq + bh * (long)N * dk;
+        double *dkb = dk_out + bh * (long)N * dk;
+        double *dvb = dv_out + bh * (long)N * dv;
+        double *Sp = calloc((size_t)dk * dv1, sizeof(double)); /* S' */
+        double *Rp = calloc((size_t)dk * dv1, sizeof(double)); /* R' */
+        double *Gi = malloc((size_t)dv1 * sizeof(double));      /* G'_i */
+
+        /* S' over all tokens. */
+        for (int j = 0; j < N; ++j) {
+            for (int e = 0; e < dk; ++e) {
+                double fk = phi(kb[(long)j * dk + e]);
+                for (int c = 0; c < dv; ++c) Sp[(long)e * dv1 + c] += fk * vb[(long)j * dv + c];
+                Sp[(long)e * dv1 + dv] += fk;
+            }
+        }
+        /* Per query: den_i, out_i, G'_i; dq_i = (S' G'_i) * phi'(q_i); R' += phi(q_i) G'_i^T. */
+        for (int i = 0; i < N; ++i) {
+            double d = 0.0;
+            for (int e = 0; e < dk; ++e) d += phi(qb[(long)i * dk + e]) * Sp[(long)e * dv1 + dv];
+            double go = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < dk; ++e) num += phi(qb[(long)i * dk + e]) * Sp[(long)e * dv1 + c];
+                go += gb[(long)i * dv + c] * (num / d);
+                Gi[c] = gb[(long)i * dv + c] / d;
+            }
+            Gi[dv] = -go / d;
+            for (int e = 0; e < dk; ++e) {
+                double acc = 0.0;
+                for (int c = 0; c < dv1; ++c) acc += Sp[(long)e * dv1 + c] * Gi[c];
+                dqb[(long)i * dk + e] = acc * dphi(qb[(long)i * dk + e]);
+                double fq = phi(qb[(long)i * dk + e]);
+                for (int c = 0; c < dv1; ++c) Rp[(long)e * dv1 + c] += fq * Gi[c];
+            }
+        }
+        /* Per key: dk_j = (R' V'_j) * phi'(k_j), dv_j = R^T phi(k_j). */
+        for (int j = 0; j < N; ++j) {
+            for (int e = 0; e < dk; ++e) {
+                double acc = Rp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */
+                for (int c = 0; c < dv; ++c) acc += Rp[(long)e * dv1 + c] * vb[(long)j * dv + c];
+                dkb[(long)j * dk + e] = acc * dphi(kb[(long)j * dk + e]);
+            }
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int e = 0; e < dk; ++e) acc += Rp[(long)e * dv1 + c] * phi(kb[(long)j * dk + e]);
+                dvb[(long)j * dv + c] = acc;
+            }
+        }
+        free(Sp);
+        free(Rp);
+        free(Gi);
+    }
+}

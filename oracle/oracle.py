@@ -42,6 +42,7 @@ def _bind(path: str):
     lib.oracle_fwd_noncausal_f64.argtypes = [P, P, P, P, i, i, i, i, i]
     lib.oracle_decode_step_f64.argtypes = [P, P, P, P, P, P, i, i, i, i]
     lib.oracle_bwd_causal_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
+    lib.oracle_bwd_noncausal_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -120,6 +121,20 @@ def bwd_causal(q, k, v, dout, lib=None):
     dvv = np.empty_like(v)
     (lib or _load()).oracle_bwd_causal_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dkk), _ptr(dvv),
                                   B, H, N, dk, dv)
+    return dq, dkk, dvv
+
+
+def bwd_noncausal(q, k, v, dout, lib=None):
+    """Exact gradient of the non-causal forward: returns (dq, dk, dv)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    assert g.shape == v.shape
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    (lib or _load()).oracle_bwd_noncausal_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dkk), _ptr(dvv),
+                                     B, H, N, dk, dv)
     return dq, dkk, dvv
 
 

@@ -38,6 +38,7 @@ def example(name, q, k, v, g, note):
     den_c = exact.denominators(q, k, causal=True)
     out_n = exact.attention(q, k, v, causal=False)
     dq, dk, dv = exact.gradients(q, k, v, g, causal=True)
+    ndq, ndk, ndv = exact.gradients(q, k, v, g, causal=False)
     doc = {
         "citation": CITATION,
         "note": note,
@@ -46,6 +47,7 @@ def example(name, q, k, v, g, note):
         "causal_out": mat(out_c), "causal_den": [s(x) for x in den_c],
         "noncausal_out": mat(out_n),
         "causal_dq": mat(dq), "causal_dk": mat(dk), "causal_dv": mat(dv),
+        "noncausal_dq": mat(ndq), "noncausal_dk": mat(ndk), "noncausal_dv": mat(ndv),
     }
     with open(os.path.join(HERE, name), "w") as f:
         json.dump(doc, f, indent=1, ensure_ascii=False)

@@ -57,6 +57,10 @@ def check_golden(lib=None):
         np.testing.assert_allclose(dq, _frac_array(ex["causal_dq"]), rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(dk, _frac_array(ex["causal_dk"]), rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(dv, _frac_array(ex["causal_dv"]), rtol=1e-12, atol=1e-14)
+        ndq, ndk, ndv = oracle.bwd_noncausal(q, k, v, g, lib=lib)
+        np.testing.assert_allclose(ndq, _frac_array(ex["noncausal_dq"]), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(ndk, _frac_array(ex["noncausal_dk"]), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(ndv, _frac_array(ex["noncausal_dv"]), rtol=1e-12, atol=1e-14)
 
 
 def check_causal_vs_quadratic(lib=None):
@@ -164,8 +168,46 @@ def check_backward(lib=None):
     assert np.abs(dq0).max() < 1e-12 and np.abs(dk0).max() < 1e-12
 
 
+def check_backward_noncausal(lib=None):
+    """Non-causal oracle gradient == central finite differences of the quadratic
+    form; value gradients sum to the upstream gradients; equal values give zero
+    dq, dk; a joint permutation of the K and V rows permutes dk and dv and leaves
+    dq unchanged; at N = 1 it equals the causal gradient."""
+    B, H, N, dk, dv = 1, 2, 8, 3, 4
+    q, k, v = _qkv(B, H, N, dk, dv, seed=21)
+    g = _rng(22).standard_normal(v.shape)
+    dq, dkk, dvv = oracle.bwd_noncausal(q, k, v, g, lib=lib)
+
+    def loss_q(x):
+        return float((forms.noncausal_quadratic(x, k, v) * g).sum())
+
+    def loss_k(x):
+        return float((forms.noncausal_quadratic(q, x, v) * g).sum())
+
+    def loss_v(x):
+        return float((forms.noncausal_quadratic(q, k, x) * g).sum())
+
+    for got, f, x in ((dq, loss_q, q), (dkk, loss_k, k), (dvv, loss_v, v)):
+        ref = forms.fd_gradient(f, x.copy())
+        err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+        assert err < 1e-6, f"finite-difference mismatch {err:.3e}"
+    np.testing.assert_allclose(dvv.sum(2), g.sum(2), rtol=1e-12, atol=1e-12)
+    veq = np.broadcast_to(_rng(23).standard_normal(dv), v.shape).copy()
+    dq0, dk0, _ = oracle.bwd_noncausal(q, k, veq, g, lib=lib)
+    assert np.abs(dq0).max() < 1e-12 and np.abs(dk0).max() < 1e-12
+    perm = _rng(24).permutation(N)
+    pq, pk, pv = oracle.bwd_noncausal(q, k[:, :, perm], v[:, :, perm], g, lib=lib)
+    np.testing.assert_allclose(pq, dq, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(pk, dkk[:, :, perm], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(pv, dvv[:, :, perm], rtol=1e-12, atol=1e-13)
+    q1, k1, v1 = _qkv(2, 1, 1, 5, 3, seed=25)
+    g1 = _rng(26).standard_normal(v1.shape)
+    for a, b in zip(oracle.bwd_noncausal(q1, k1, v1, g1, lib=lib), oracle.bwd_causal(q1, k1, v1, g1, lib=lib)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
 ALL_CHECKS = [check_golden, check_causal_vs_quadratic, check_causal_vs_chunked, check_noncausal,
-              check_invariants, check_decode, check_backward]
+              check_invariants, check_decode, check_backward, check_backward_noncausal]
 
 
 def failing_checks(lib):

@@ -60,6 +60,15 @@ MUTANTS = {
                       "for (int e = 0; e < dk; ++e) acc += Sp[(long)e * dv1 + c] * phi(qb[(long)j * dk + e]);"),
     "bwd_dq_missing_chain_rule": ("dqb[(long)i * dk + e] = acc * dphi(qb[(long)i * dk + e]);",
                                   "dqb[(long)i * dk + e] = acc;"),
+    "nbwd_eps_sign": ("Gi[dv] = -go / d;", "Gi[dv] = go / d;"),
+    "nbwd_drops_ones_column": ("double acc = Rp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */",
+                               "double acc = 0.0;"),
+    "nbwd_R_from_k": ("double fq = phi(qb[(long)i * dk + e]);\n                for (int c = 0; c < dv1; ++c) Rp",
+                      "double fq = phi(kb[(long)i * dk + e]);\n                for (int c = 0; c < dv1; ++c) Rp"),
+    "nbwd_dv_transposed": ("acc += Rp[(long)e * dv1 + c] * phi(kb[(long)j * dk + e]);",
+                           "acc += Rp[(long)(c % dk) * dv1 + (e % dv)] * phi(kb[(long)j * dk + e]);"),
+    "nbwd_dq_drops_normaliser_term": ("for (int c = 0; c < dv1; ++c) acc += Sp[(long)e * dv1 + c] * Gi[c];",
+                                      "for (int c = 0; c < dv; ++c) acc += Sp[(long)e * dv1 + c] * Gi[c];"),
 }
 
 
