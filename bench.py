@@ -219,8 +219,18 @@ def bench_noncausal(dev, steps=100, warmup=20, B=4, H=8, N=4096, d=64, seed=0):
     ws = torch.empty(max(1, la.la_fwd_noncausal_workspace_bytes(B, H, N, d, d)), dtype=torch.uint8, device=dev)
     ms = time_calls(lambda: la.la_fwd_noncausal(q, k, v, o=o, ws=ws), steps, warmup, torch.cuda.current_stream(dev))
     by = B * H * N * 4 * d * 2
-    return {"workload": f"noncausal_fwd_bf16_B{B}_H{H}_N{N}_d{d}", "us": round(ms * 1e3, 3),
-            "achieved_GBs": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res = {"workload": f"noncausal_fwd_bf16_B{B}_H{H}_N{N}_d{d}", "us": round(ms * 1e3, 3),
+           "achieved_GBs": round(by / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # its backward at the same shape: q, k, v, dO read, dq, dk, dv written
+    dO = inputs.to_torch(inputs.attention_inputs(B, H, N, d, d, seed=seed, with_grad=True)["dO"], torch.bfloat16, dev)
+    wsb = torch.empty(max(1, la.la_bwd_noncausal_workspace_bytes(B, H, N, d, d)), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    bms = time_calls(lambda: la.la_bwd_noncausal(q, k, v, dO, dq=dq, dk=dk, dv=dv, ws=wsb), steps, warmup,
+                     torch.cuda.current_stream(dev))
+    bby = B * H * N * 7 * d * 2
+    res.update({"bwd_us": round(bms * 1e3, 3), "bwd_GBs": round(bby / (bms * 1e-3) / 1e9, 1),
+                "bwd_hbm_frac": round(bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    return res
 
 
 def bench_bwd(dev, steps=20, warmup=20, B=8, H=16, N=8192, d=128, C=64, seed=0):

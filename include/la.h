@@ -80,6 +80,7 @@ const char *la_status_string(la_status s);
 size_t la_fwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C);
 size_t la_fwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v);
 size_t la_bwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C);
+size_t la_bwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v);
 
 /*
  * Non-causal forward: o_i = phi(q_i)^T (sum_j phi(k_j) v_j^T) /
@@ -139,6 +140,25 @@ la_status la_bwd_causal(const void *q, const void *k, const void *v, const void 
                         void *dq, void *dk, void *dv,
                         int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of the non-causal form (blog digest "Method / key components 2)";
+ * velog 3.2 for the form, 3.5 for the gradient as sums with linear memory):
+ * the exact gradient of la_fwd_noncausal with respect to q, k and v for an
+ * upstream gradient dO.  The formulas are those of la_bwd_causal with the
+ * prefix and suffix sums replaced by full sums over all N tokens:
+ *   dphi(q_i) = S gh_i + eps_i z,  S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j)
+ *   dphi(k_j) = R v_j + r,  dv_j = R^T phi(k_j),
+ *   R = sum_i phi(q_i) gh_i^T, r = sum_i phi(q_i) eps_i,
+ * then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).  Layouts, dtypes and
+ * errors as la_bwd_causal; there is no C argument (the tiling is internal).
+ * The workspace (always required) holds two floats per token and
+ * per-segment d_k x (d_v + 1) partial sums.
+ */
+la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const void *dO,
+                           void *dq, void *dk, void *dv,
+                           int B, int H, int N, int d_k, int d_v, la_dtype in,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * One recurrent decode step for every (b, h):

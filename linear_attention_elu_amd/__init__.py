@@ -9,9 +9,11 @@ from .binding import (  # noqa: F401
     la_fwd_causal_workspace_bytes,
     la_fwd_noncausal_workspace_bytes,
     la_bwd_causal_workspace_bytes,
+    la_bwd_noncausal_workspace_bytes,
     la_fwd_causal,
     la_fwd_causal_state,
     la_fwd_noncausal,
     la_bwd_causal,
+    la_bwd_noncausal,
     la_decode_step,
 )

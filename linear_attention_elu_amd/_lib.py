@@ -23,10 +23,12 @@ EXPORTS = (
     "la_fwd_causal_workspace_bytes",
     "la_fwd_noncausal_workspace_bytes",
     "la_bwd_causal_workspace_bytes",
+    "la_bwd_noncausal_workspace_bytes",
     "la_fwd_noncausal",
     "la_fwd_causal",
     "la_fwd_causal_state",
     "la_bwd_causal",
+    "la_bwd_noncausal",
     "la_decode_step",
 )
 
@@ -69,6 +71,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_fwd_causal_state.restype = i
     lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_causal.restype = i
+    lib.la_bwd_noncausal_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.la_bwd_noncausal_workspace_bytes.restype = sz
+    lib.la_bwd_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_bwd_noncausal.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i
     if path is None:

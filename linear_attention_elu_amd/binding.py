@@ -74,6 +74,10 @@ def la_bwd_causal_workspace_bytes(B: int, H: int, N: int, d_k: int, d_v: int, C:
     return int(_lib.load().la_bwd_causal_workspace_bytes(B, H, N, d_k, d_v, C))
 
 
+def la_bwd_noncausal_workspace_bytes(B: int, H: int, N: int, d_k: int, d_v: int) -> int:
+    return int(_lib.load().la_bwd_noncausal_workspace_bytes(B, H, N, d_k, d_v))
+
+
 def _shapes(q, k, v):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError(f"expected q, k [B,H,N,d_k] and v [B,H,N,d_v]; got {tuple(q.shape)}, "
@@ -163,6 +167,26 @@ def la_bwd_causal(q, k, v, dO, dq=None, dk=None, dv=None, C: int = 64, ws=None, 
     rc = _lib.load().la_bwd_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
                                    B, H, N, d_k, d_v, C, _code(q), wp, wb, _stream(dev, stream))
     _lib.check(rc, "la_bwd_causal")
+    return dq, dk, dv
+
+
+def la_bwd_noncausal(q, k, v, dO, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Backward of the non-causal forward.  Returns (dq, dk, dv) in the dtype of q."""
+    B, H, N, d_k, d_v = _shapes(q, k, v)
+    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
+    if tuple(dO.shape) != (B, H, N, d_v) or dO.dtype != q.dtype:
+        raise ValueError("dO must be [B,H,N,d_v] in the dtype of q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("dq, dk, dv must match q, k, v in shape and dtype")
+    _dev(dq, dk, dv)
+    wp, wb = _ws(la_bwd_noncausal_workspace_bytes(B, H, N, d_k, d_v), dev, ws)
+    rc = _lib.load().la_bwd_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      B, H, N, d_k, d_v, _code(q), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_bwd_noncausal")
     return dq, dk, dv
 
 

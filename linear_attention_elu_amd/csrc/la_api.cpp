@@ -116,6 +116,11 @@ size_t la_bwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int 
     return la::bwd_workspace_bytes(B, H, N, d_k, d_v, C);
 }
 
+size_t la_bwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v) {
+    if (B < 1 || H < 1 || N < 1 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    return la::bwd_workspace_bytes(B, H, N, d_k, d_v, kNonCausalChunk);
+}
+
 la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void *o, float *den,
                               const float *S0, const float *z0, float *S_out, float *z_out,
                               int B, int H, int N, int d_k, int d_v, int C,
@@ -179,6 +184,25 @@ la_status la_bwd_causal(const void *q, const void *k, const void *v, const void 
     const size_t need = la::bwd_workspace_bytes(B, H, N, d_k, d_v, C);
     if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
     la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream};
+    return from_hip(la::run_bwd(d));
+}
+
+la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const void *dO,
+                           void *dq, void *dk, void *dv,
+                           int B, int H, int N, int d_k, int d_v, la_dtype in,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !dO || !dq || !dk || !dv) return LA_ERR_NULL_PTR;
+    la_status st = check_shape(B, H, N);
+    if (st != LA_OK) return st;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in)) return LA_ERR_BAD_DTYPE;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(dO) || !aligned(dq) || !aligned(dk) ||
+        !aligned(dv) || !aligned_or_null(ws))
+        return LA_ERR_ALIGNMENT;
+    const size_t need = la::bwd_workspace_bytes(B, H, N, d_k, d_v, kNonCausalChunk);
+    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, kNonCausalChunk, in == LA_BF16,
+                  static_cast<float *>(ws), stream, 1};
     return from_hip(la::run_bwd(d));
 }
 

@@ -43,6 +43,12 @@
 // and value block w of dv, which needs R contracted over features: a copy of
 // R in LDS, read with the transpose read.
 //
+// Non-causal form (NC = true; blog digest "Method / key components 2)"):
+// the same gradient with full sums instead of prefix and suffix sums, so every
+// token reads the totals S, z (dq sweep) and R, r (dk/dv sweep): no masked
+// in-chunk products, no carry, and each sweep loads only the rows it needs
+// (q, dO for dq; k, v for dk, dv).
+//
 // LDS row strides: tiles read row-wise (two 8-byte pieces per lane, rows p =
 // 0..15) are padded to a stride of 4 (mod 8) times an odd number of banks,
 // tiles read with the transpose read (rows 4g..4g+3 per lane group) to 8
@@ -173,7 +179,7 @@ template <int DK, int DV, typename TI> struct DqSmem {
     alignas(16) float red[kBwdWaves][CM][2];  // per-wave partial phi(q).X and phi(q).z
 };
 
-template <int DK, int DV, typename TI>
+template <int DK, int DV, typename TI, bool NC = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dq_kernel(const BwdParams p) {
     using TC = TI;
@@ -219,10 +225,17 @@ la_bwd_dq_kernel(const BwdParams p) {
             for (int r = 0; r < 4; ++r) accS[cv][r] = Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
     }
     Frag<TC> fragS[NSV];  // S rows e, split over the value index
+    // Non-causal with bf16 operands: the total S also as its rounding
+    // remainder, so that X = S g and z meet at fp32-level accuracy in
+    // X - z (phi(q) . X) / den, whose two terms cancel exactly for a single token.
+    constexpr bool SLO = NC && sizeof(TC) == 2;
+    Frag<TC> fragS_lo[SLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
-        for (int s = 0; s < NSV; ++s)
+        for (int s = 0; s < NSV; ++s) {
             acc_to_frag(fragS[s], accS[2 * s], (2 * s + 1 < CV) ? accS[2 * s + 1] : zero4);
+            if constexpr (SLO) acc_to_frag_lo(fragS_lo[s], accS[2 * s], (2 * s + 1 < CV) ? accS[2 * s + 1] : zero4);
+        }
     };
     refresh();
     Frag<TC> ones;
@@ -233,14 +246,14 @@ la_bwd_dq_kernel(const BwdParams p) {
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        xk.load(p.k, bh * N, r0, nrows, tid);
+        if constexpr (!NC) xk.load(p.k, bh * N, r0, nrows, tid);
         xq.load(p.q, bh * N, r0, nrows, tid);
-        xv.load(p.v, bh * N, r0, nrows, tid);
+        if constexpr (!NC) xv.load(p.v, bh * N, r0, nrows, tid);
         xg.load(p.g, bh * N, r0, nrows, tid);
     };
     if (nch > 0) {
         fetch(0);
-        xk.apply_phi();
+        if constexpr (!NC) xk.apply_phi();
         xq.apply_phi();
     }
 
@@ -257,14 +270,14 @@ la_bwd_dq_kernel(const BwdParams p) {
         __syncthreads();  // previous chunk's tile reads done
         // (phi(k), phi(q) were applied in registers during the previous chunk)
         if (nrows == SM::CM) {
-            xk.template store<SM::LK, true>(sm.k, nrows, tid);
+            if constexpr (!NC) xk.template store<SM::LK, true>(sm.k, nrows, tid);
             xq.template store<SM::LQ, true>(sm.q, nrows, tid);
-            xv.template store<SM::LV, true>(sm.v, nrows, tid);
+            if constexpr (!NC) xv.template store<SM::LV, true>(sm.v, nrows, tid);
             xg.template store<SM::LG, true>(sm.g, nrows, tid);
         } else {
-            xk.template store<SM::LK, false>(sm.k, nrows, tid);
+            if constexpr (!NC) xk.template store<SM::LK, false>(sm.k, nrows, tid);
             xq.template store<SM::LQ, false>(sm.q, nrows, tid);
-            xv.template store<SM::LV, false>(sm.v, nrows, tid);
+            if constexpr (!NC) xv.template store<SM::LV, false>(sm.v, nrows, tid);
             xg.template store<SM::LG, false>(sm.g, nrows, tid);
         }
         __syncthreads();
@@ -272,7 +285,7 @@ la_bwd_dq_kernel(const BwdParams p) {
 
         // Masked M_ij = g_i . v_j (j <= i) over the blocks I >= J, one block
         // per wave and pass; blocks above the diagonal stay zero in LDS.
-        for (int b = wave; b < nib * (nib + 1) / 2; b += NW) {
+        for (int b = wave; !NC && b < nib * (nib + 1) / 2; b += NW) {
             int I, J;
             lower_block(b, I, J);
             f32x4 acc = zero4;
@@ -299,7 +312,7 @@ la_bwd_dq_kernel(const BwdParams p) {
         if (active) {
 #pragma unroll
             for (int jp = 0; jp < NTS; ++jp)
-                lds_frag_tr(fkt[jp], sm.k, SM::LK, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g, 16 * eb, pp);
+                if constexpr (!NC) lds_frag_tr(fkt[jp], sm.k, SM::LK, 32 * jp + 4 * g, 32 * jp + 16 + 4 * g, 16 * eb, pp);
 #pragma unroll
             for (int I = 0; I < NIB; ++I) {
                 X[I] = zero4;
@@ -311,7 +324,7 @@ la_bwd_dq_kernel(const BwdParams p) {
                     f32x4 ax = zero4, az = accZ;
 #pragma unroll
                     for (int jp = 0; jp < NTS; ++jp) {
-                        if (2 * jp <= I) {
+                        if (!NC && 2 * jp <= I) {
                             Frag<TC> fm, ftr;
                             lds_frag_split_v(fm, mhb, 16 * I * SM::LM + 32 * jp);
                             ax = mma(fkt[jp], fm, ax);
@@ -329,7 +342,10 @@ la_bwd_dq_kernel(const BwdParams p) {
                         }
                     }
 #pragma unroll
-                    for (int s = 0; s < NSV; ++s) ax = mma(fragS[s], fg[s], ax);
+                    for (int s = 0; s < NSV; ++s) {
+                        ax = mma(fragS[s], fg[s], ax);
+                        if constexpr (SLO) ax = mma(fragS_lo[s], fg[s], ax);
+                    }
                     const f32x4 fq = lds_get4(qb, 16 * I * SM::LQ);
                     float px = 0.f, pz = 0.f;
 #pragma unroll
@@ -378,9 +394,9 @@ la_bwd_dq_kernel(const BwdParams p) {
             }
         }
         // phi of the next chunk's rows (after the last chunk the registers are not used again)
-        xk.apply_phi();
+        if constexpr (!NC) xk.apply_phi();
         xq.apply_phi();
-        if (active) {
+        if (active && !NC) {
             // state carry: S^T(c', eb) += V^T(c') phi(K)(eb), z(eb) += phi(K)(eb)^T 1
             // (token rows past the chunk are zero in the tiles)
 #pragma unroll
@@ -423,7 +439,7 @@ template <int DK, int DV, typename TI> struct DkvSmem {
     alignas(16) float a[CM];  // a = 1 / den
 };
 
-template <int DK, int DV, typename TI>
+template <int DK, int DV, typename TI, bool NC = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dkdv_kernel(const BwdParams p) {
     using TC = TI;
@@ -461,8 +477,9 @@ la_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int cv = 0; cv < CV; ++cv) accR[cv] = zero4;
     if (p.state && has_e) {
-        // suffix state after this segment: the exclusive suffix of its last fine segment
-        const long last = min((long)(seg + 1) * p.state_mult, (long)p.state_P) - 1;
+        // suffix state after this segment: the exclusive suffix of its last fine
+        // segment (non-causal: the total, in slot 0)
+        const long last = NC ? 0 : min((long)(seg + 1) * p.state_mult, (long)p.state_P) - 1;
         const float *Rin = p.state + (bh * p.state_P + last) * (long)(DK * DV + DK);
 #pragma unroll
         for (int r = 0; r < 4; ++r) accr[r] = Rin[DK * DV + 16 * eb + 4 * g + r];
@@ -472,10 +489,16 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             for (int r = 0; r < 4; ++r) accR[cv][r] = Rin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
     }
     Frag<TC> fragR[NSV];  // R rows e, split over the value index
+    // Non-causal with bf16 operands: R also as its rounding remainder, so that
+    // R v_j and r meet at fp32-level accuracy (they cancel for a single token).
+    constexpr bool RLO = NC && sizeof(TC) == 2;
+    Frag<TC> fragR_lo[RLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
-        for (int s = 0; s < NSV; ++s)
+        for (int s = 0; s < NSV; ++s) {
             acc_to_frag(fragR[s], accR[2 * s], (2 * s + 1 < CV) ? accR[2 * s + 1] : zero4);
+            if constexpr (RLO) acc_to_frag_lo(fragR_lo[s], accR[2 * s], (2 * s + 1 < CV) ? accR[2 * s + 1] : zero4);
+        }
 #pragma unroll
         for (int cv = 0; cv < CV; ++cv) lds_put4(&sm.R[(16 * eb + pp) * SM::LR + 16 * cv + 4 * g], accR[cv]);
     };
@@ -487,11 +510,11 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        xq.load(p.q, bh * N, r0, nrows, tid);
+        if constexpr (!NC) xq.load(p.q, bh * N, r0, nrows, tid);
         xk.load(p.k, bh * N, r0, nrows, tid);
         xv.load(p.v, bh * N, r0, nrows, tid);
-        xg.load(p.g, bh * N, r0, nrows, tid);
-        if (tid < SM::CM) {
+        if constexpr (!NC) xg.load(p.g, bh * N, r0, nrows, tid);
+        if (!NC && tid < SM::CM) {
             const long t = bh * N + r0 + min(tid, nrows - 1);
             xe = p.eps[t];
             xa = p.inv_den[t];
@@ -499,7 +522,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     };
     if (nch > 0) {
         fetch(nch - 1);
-        xq.apply_phi();
+        if constexpr (!NC) xq.apply_phi();
         xk.apply_phi();
     }
 
@@ -518,17 +541,17 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         __syncthreads();  // previous chunk's tile reads done
         // (phi(q), phi(k) were applied in registers during the previous chunk)
         if (nrows == SM::CM) {
-            xq.template store<SM::LQ, true>(sm.q, nrows, tid);
+            if constexpr (!NC) xq.template store<SM::LQ, true>(sm.q, nrows, tid);
             xk.template store<SM::LK, true>(sm.k, nrows, tid);
             xv.template store<SM::LV, true>(sm.v, nrows, tid);
-            xg.template store<SM::LG, true>(sm.g, nrows, tid);
+            if constexpr (!NC) xg.template store<SM::LG, true>(sm.g, nrows, tid);
         } else {
-            xq.template store<SM::LQ, false>(sm.q, nrows, tid);
+            if constexpr (!NC) xq.template store<SM::LQ, false>(sm.q, nrows, tid);
             xk.template store<SM::LK, false>(sm.k, nrows, tid);
             xv.template store<SM::LV, false>(sm.v, nrows, tid);
-            xg.template store<SM::LG, false>(sm.g, nrows, tid);
+            if constexpr (!NC) xg.template store<SM::LG, false>(sm.g, nrows, tid);
         }
-        if (tid < SM::CM) {
+        if (!NC && tid < SM::CM) {
             sm.e[tid] = tid < nrows ? xe : 0.f;
             sm.a[tid] = tid < nrows ? xa : 0.f;
         }
@@ -539,7 +562,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         //   M_ij = (g_i . v_j + e_i) a_i,  A_ij = (phi(q_i) . phi(k_j)) a_i  (i >= j),
         // stored transposed, [j][i]; blocks above the diagonal stay zero in LDS.
         const int nblk = nib * (nib + 1) / 2;
-        for (int b = wave; b < 2 * nblk; b += NW) {
+        for (int b = wave; !NC && b < 2 * nblk; b += NW) {
             const bool is_a = b >= nblk;
             int I, J;
             lower_block(is_a ? b - nblk : b, I, J);
@@ -585,12 +608,12 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         __syncthreads();  // M and A blocks are in LDS; R copy reads done
 
         Frag<TC> fqt[NTS], fgt[NTS];  // phi(Q) (features 16 eb + pp), dO (values 16 cb + pp) over queries
-        if (has_e) {
+        if (has_e && !NC) {
 #pragma unroll
             for (int ip = 0; ip < NTS; ++ip)
                 lds_frag_tr(fqt[ip], sm.q, SM::LQ, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * eb, pp);
         }
-        if (has_c) {
+        if (has_c && !NC) {
 #pragma unroll
             for (int ip = 0; ip < NTS; ++ip)
                 lds_frag_tr(fgt[ip], sm.g, SM::LG, 32 * ip + 4 * g, 32 * ip + 16 + 4 * g, 16 * cb, pp);
@@ -606,7 +629,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     f32x4 acc = zero4;
 #pragma unroll
                     for (int ip = 0; ip < NTS; ++ip) {
-                        if (2 * ip + 1 >= J) {
+                        if (!NC && 2 * ip + 1 >= J) {
                             Frag<TC> fm;
                             lds_frag_split_v(fm, mhb, 16 * J * SM::LM + 32 * ip);
                             acc = mma(fqt[ip], fm, acc);
@@ -621,6 +644,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                         Frag<TC> fv;
                         lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
                         acc = mma(fragR[s], fv, acc);
+                        if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
                     }
                     const f32x4 kd = lds_get4(kb, 16 * J * SM::LK + 16 * eb);
                     f32x4 out;
@@ -633,7 +657,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     f32x4 acc = zero4;
 #pragma unroll
                     for (int ip = 0; ip < NTS; ++ip) {
-                        if (2 * ip + 1 >= J) {
+                        if (!NC && 2 * ip + 1 >= J) {
                             Frag<TC> fa;
                             lds_frag_split_v(fa, atb, 16 * J * SM::LM + 32 * ip);
                             acc = mma(fgt[ip], fa, acc);
@@ -650,9 +674,9 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             }
         }
         // phi of the previous chunk's rows (after the first chunk the registers are not used again)
-        xq.apply_phi();
+        if constexpr (!NC) xq.apply_phi();
         xk.apply_phi();
-        if (has_e) {
+        if (has_e && !NC) {
             // state carry: R^T(c', eb) += dO^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
             // (a = 0 for token rows past the chunk)
 #pragma unroll

@@ -29,8 +29,101 @@ inline BwdLayout bwd_layout(long BH, int N, int DK, int DV, int Pmax) {
     return l;
 }
 
+// Gradient of the non-causal form: the totals S, z and R, r replace the
+// prefix and suffix states, so the sequence splits freely.
+//   aggregates of phi(K)^T V, phi(K)^T 1 per segment -> total
+//   dq sweep (non-causal)      leaves 1/den and eps per token
+//   aggregates of (phi(Q)/den)^T dO, (phi(Q)/den)^T e per segment -> total
+//   dk/dv sweep (non-causal)
+template <int DK, int DV, typename TI, int CT>
+hipError_t run_bwd_nc_ct(const BwdDesc &d) {
+    const long BH = (long)d.B * d.H;
+    int Lmax = 0;
+    const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);
+    const BwdLayout lay = bwd_layout(BH, d.N, DK, DV, Pmax);
+    char *ws = reinterpret_cast<char *>(d.ws);
+    float *inv_den = reinterpret_cast<float *>(ws + lay.inv_den);
+    float *eps = reinterpret_cast<float *>(ws + lay.eps);
+    float *tot = reinterpret_cast<float *>(ws + lay.pre);
+    float *rtot = reinterpret_cast<float *>(ws + lay.suf);
+    hipError_t err;
+
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT, false>;
+    auto aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, CT, false>;
+    auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI, true>;
+    auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI, true>;
+    static OccCache occ_dq, occ_kv;
+    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT>();
+    const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), occ_dq, kBwdThreads);
+    const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
+    int Lf = 0;
+    const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
+
+    FwdParams a{};
+    a.N = d.N;
+    a.L = Lf;
+    a.state_P = Pf;
+    a.state_mult = 1;
+    a.k = d.k;
+    a.v = d.v;
+    a.seg_out = tot;
+    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (Pf > 1 && (err = launch_seg_scan(tot, nullptr, nullptr, BH, Pf, DK, DV, 1, Pf, d.stream)) != hipSuccess)
+        return err;
+
+    BwdParams b{};
+    b.q = d.q;
+    b.k = d.k;
+    b.v = d.v;
+    b.g = d.dO;
+    b.inv_den = inv_den;
+    b.eps = eps;
+    b.dq = d.dq;
+    b.dk = d.dk;
+    b.dv = d.dv;
+    b.N = d.N;
+    b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
+    b.state_P = Pf;
+    b.state_mult = 0;  // every segment reads the total in slot 0
+    int Lq = 0, Lkv = 0;
+    const int Pq = plan_segments(BH, d.N, d.C, target_dq, &Lq);
+    const int Pkv = plan_segments(BH, d.N, d.C, target_kv, &Lkv);
+
+    b.state = tot;
+    b.L = Lq;
+    dq_kernel<<<dim3((unsigned)BH, (unsigned)Pq), kBwdThreads, 0, d.stream>>>(b);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    a.k = d.q;  // (a phi(Q))^T dO and (a phi(Q))^T e, a = 1 / den
+    a.v = d.dO;
+    a.kscale = inv_den;
+    a.zw = eps;
+    a.seg_out = rtot;
+    aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (Pf > 1 && (err = launch_seg_scan(rtot, nullptr, nullptr, BH, Pf, DK, DV, 1, Pf, d.stream)) != hipSuccess)
+        return err;
+
+    b.state = rtot;
+    b.L = Lkv;
+    dkdv_kernel<<<dim3((unsigned)BH, (unsigned)Pkv), kBwdThreads, 0, d.stream>>>(b);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, typename TI>
+hipError_t run_bwd_nc_t(const BwdDesc &d) {
+    switch (fwd_chunk<DK, DV, TI>(d.C)) {
+        case 16: return run_bwd_nc_ct<DK, DV, TI, 16>(d);
+        case 32: return run_bwd_nc_ct<DK, DV, TI, 32>(d);
+        case 64: return run_bwd_nc_ct<DK, DV, TI, 64>(d);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int DK, int DV, typename TI>
 hipError_t run_bwd_t(const BwdDesc &d) {
+    if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);
     const long BH = (long)d.B * d.H;
     int Lmax = 0;
     const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);

@@ -310,6 +310,18 @@ __device__ __forceinline__ void acc_to_frag(Frag<TC> &f, const f32x4 &lo, const 
     }
 }
 
+// The rounding remainder of acc_to_frag: slot values x - TC(x), rounded to TC
+// (zero for fp32 operands).  A product with f plus one with this remainder
+// reproduces the fp32 accumulator values to about 16 significant bits.
+template <typename TC>
+__device__ __forceinline__ void acc_to_frag_lo(Frag<TC> &f, const f32x4 &lo, const f32x4 &hi) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f.set(t, lo[t] - to_operand<TC>(lo[t]));
+        f.set(t + 4, hi[t] - to_operand<TC>(hi[t]));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Global memory element access for the two storage types.
 // ---------------------------------------------------------------------------

@@ -38,6 +38,7 @@ struct BwdDesc {
     int in_bf16;
     float *ws;
     hipStream_t stream;
+    int noncausal;  // gradient of the non-causal form (full sums)
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a

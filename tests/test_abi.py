@@ -131,6 +131,35 @@ def test_bwd_causal_rejects(lib):
     assert f(*bad) == 5
 
 
+def test_bwd_noncausal_rejects(lib):
+    f = lib.la_bwd_noncausal
+    need = la.la_bwd_noncausal_workspace_bytes(1, 1, 64, 64, 64)
+    assert need > 0
+    assert la.la_bwd_noncausal_workspace_bytes(1, 1, 64, 48, 64) == 0
+    args = [P] * 7 + [1, 1, 64, 64, 64, 1, P, need, None]
+    bad = list(args)
+    bad[0] = None  # q
+    assert f(*bad) == 1
+    bad = list(args)
+    bad[9] = 0  # N
+    assert f(*bad) == 2
+    bad = list(args)
+    bad[10] = 24  # d_k
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[12] = 9  # dtype
+    assert f(*bad) == 4
+    bad = list(args)
+    bad[4] = MIS  # dq
+    assert f(*bad) == 7
+    bad = list(args)
+    bad[13] = None  # the workspace is always required
+    assert f(*bad) == 5
+    bad = list(args)
+    bad[14] = need - 1
+    assert f(*bad) == 5
+
+
 def test_decode_rejects(lib):
     f = lib.la_decode_step
     assert f(None, P, P, P, P, P, 1, 1, 32, 32, 0, None) == 1
