@@ -11,6 +11,8 @@ from .oracle import (  # noqa: F401
     decode_step,
     bwd_causal,
     bwd_noncausal,
+    fwd_causal_decay,
+    decode_step_decay,
     num_threads,
     library_path,
     load_variant,

@@ -362,3 +362,86 @@ void oracle_bwd_noncausal_f64(const double *q, const double *k, const double *v,
         free(Gi);
     }
 }
+
+/*
+ * Causal forward with a fixed per-head decay gamma (the itwiki article's table
+ * of later variants, RetNet row: S_t = gamma S_{t-1} + ...).  The feature map
+ * and the normaliser of the base method are kept, and both running sums decay:
+ *   S_i = gamma_h S_{i-1} + phi(k_i) v_i^T,   z_i = gamma_h z_{i-1} + phi(k_i),
+ *   out_i = phi(q_i)^T S_i / phi(q_i) . z_i,
+ * with gamma_h = gamma[h] for head h of the (b, h) pair.  gamma = 1 is the
+ * causal form above.  `den` may be NULL.
+ */
+void oracle_fwd_causal_decay_f64(const double *q, const double *k, const double *v, const double *gamma,
+                                 double *o, double *den, int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double g = gamma[bh % H];
+        const double *qb = q + bh * (long)N * dk;
+        const double *kb = k + bh * (long)N * dk;
+        const double *vb = v + bh * (long)N * dv;
+        double *ob = o + bh * (long)N * dv;
+        double *S = calloc((size_t)dk * dv, sizeof(double));
+        double *z = calloc((size_t)dk, sizeof(double));
+        double *fq = malloc((size_t)dk * sizeof(double));
+        for (int i = 0; i < N; ++i) {
+            const double *ki = kb + (long)i * dk;
+            const double *vi = vb + (long)i * dv;
+            const double *qi = qb + (long)i * dk;
+            for (int e = 0; e < dk; ++e) {
+                double fk = phi(ki[e]);
+                z[e] = g * z[e] + fk;
+                for (int c = 0; c < dv; ++c) S[(long)e * dv + c] = g * S[(long)e * dv + c] + fk * vi[c];
+            }
+            double d = 0.0;
+            for (int e = 0; e < dk; ++e) {
+                fq[e] = phi(qi[e]);
+                d += fq[e] * z[e];
+            }
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < dk; ++e) num += fq[e] * S[(long)e * dv + c];
+                ob[(long)i * dv + c] = num / d;
+            }
+            if (den) den[bh * (long)N + i] = d;
+        }
+        free(S);
+        free(z);
+        free(fq);
+    }
+}
+
+/*
+ * One decode step with the per-head decay: S = gamma_h S + phi(k) v^T,
+ * z = gamma_h z + phi(k), then out = phi(q)^T S / phi(q) . z.
+ */
+void oracle_decode_step_decay_f64(double *S, double *z, const double *q, const double *k,
+                                  const double *v, const double *gamma, double *o,
+                                  int B, int H, int dk, int dv)
+{
+    long BH = (long)B * H;
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double g = gamma[bh % H];
+        double *Sb = S + bh * (long)dk * dv;
+        double *zb = z + bh * (long)dk;
+        const double *qb = q + bh * (long)dk;
+        const double *kb = k + bh * (long)dk;
+        const double *vb = v + bh * (long)dv;
+        double *ob = o + bh * (long)dv;
+        for (int e = 0; e < dk; ++e) {
+            double fk = phi(kb[e]);
+            zb[e] = g * zb[e] + fk;
+            for (int c = 0; c < dv; ++c) Sb[(long)e * dv + c] = g * Sb[(long)e * dv + c] + fk * vb[c];
+        }
+        double d = 0.0;
+        for (int e = 0; e < dk; ++e) d += phi(qb[e]) * zb[e];
+        for (int c = 0; c < dv; ++c) {
+            double num = 0.0;
+            for (int e = 0; e < dk; ++e) num += phi(qb[e]) * Sb[(long)e * dv + c];
+            ob[c] = num / d;
+        }
+    }
+}

@@ -43,6 +43,8 @@ def _bind(path: str):
     lib.oracle_decode_step_f64.argtypes = [P, P, P, P, P, P, i, i, i, i]
     lib.oracle_bwd_causal_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_bwd_noncausal_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
+    lib.oracle_fwd_causal_decay_f64.argtypes = [P, P, P, P, P, P, i, i, i, i, i]
+    lib.oracle_decode_step_decay_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -136,6 +138,35 @@ def bwd_noncausal(q, k, v, dout, lib=None):
     (lib or _load()).oracle_bwd_noncausal_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq), _ptr(dkk), _ptr(dvv),
                                      B, H, N, dk, dv)
     return dq, dkk, dvv
+
+
+def fwd_causal_decay(q, k, v, gamma, lib=None):
+    """Causal forward with a fixed decay gamma[h] per head.  Returns (out, den)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    g = _f64(np.asarray(gamma, dtype=np.float64).reshape(-1))
+    assert k.shape == q.shape and v.shape[:3] == (B, H, N) and g.shape == (H,)
+    o = np.empty((B, H, N, dv))
+    den = np.empty((B, H, N))
+    (lib or _load()).oracle_fwd_causal_decay_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(den),
+                                        B, H, N, dk, dv)
+    return o, den
+
+
+def decode_step_decay(S, z, q, k, v, gamma, lib=None):
+    """One decode step with a fixed decay gamma[h] per head.  Returns (S_new, z_new, out)."""
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, dk, dv = S.shape
+    g = _f64(np.asarray(gamma, dtype=np.float64).reshape(-1))
+    assert z.shape == (B, H, dk) and q.shape == (B, H, dk) and k.shape == (B, H, dk)
+    assert v.shape == (B, H, dv) and g.shape == (H,)
+    o = np.empty((B, H, dv))
+    (lib or _load()).oracle_decode_step_decay_f64(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o),
+                                         B, H, dk, dv)
+    return S, z, o
 
 
 def load_variant(path: str):

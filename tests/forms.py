@@ -34,6 +34,20 @@ def causal_quadratic(q, k, v):
     return np.matmul(a, v) / den[..., None], den
 
 
+def causal_quadratic_decay(q, k, v, gamma):
+    """Masked quadratic form with the decay mask gamma^(i - j) (j <= i), one
+    gamma per head: q, k [B, H, N, dk], v [B, H, N, dv], gamma [H]."""
+    fq, fk = phi(q), phi(k)
+    N = q.shape[-2]
+    i = np.arange(N)
+    expo = (i[:, None] - i[None, :]).astype(np.float64)
+    g = np.asarray(gamma, dtype=np.float64).reshape(1, -1, 1, 1)
+    mask = np.where(expo >= 0, g ** np.maximum(expo, 0), 0.0)
+    a = np.matmul(fq, np.swapaxes(fk, -1, -2)) * mask
+    den = a.sum(-1)
+    return np.matmul(a, v) / den[..., None], den
+
+
 def noncausal_quadratic(q, k, v):
     fq, fk = phi(q), phi(k)
     a = np.matmul(fq, np.swapaxes(fk, -1, -2))

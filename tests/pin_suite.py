@@ -206,8 +206,43 @@ def check_backward_noncausal(lib=None):
         np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
 
 
+def check_decay(lib=None):
+    """Per-head decay: gamma = 1 is the causal form; the recurrence equals the
+    quadratic form with the decay mask gamma^(i-j); gamma = 0 keeps only the
+    current token (out = v); equal value rows give that value; T decode steps
+    equal the forward; each head uses its own gamma."""
+    q, k, v = _qkv(2, 3, 40, 8, 5, seed=31)
+    gam = np.array([0.5, 0.9, 0.999])
+    o, den = oracle.fwd_causal_decay(q, k, v, gam, lib=lib)
+    ob, denb = forms.causal_quadratic_decay(q, k, v, gam)
+    np.testing.assert_allclose(o, ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(den, denb, rtol=1e-12)
+    o1, d1 = oracle.fwd_causal_decay(q, k, v, np.ones(3), lib=lib)
+    oc, dc = oracle.fwd_causal(q, k, v, lib=lib)
+    np.testing.assert_allclose(o1, oc, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(d1, dc, rtol=1e-14)
+    o0, _ = oracle.fwd_causal_decay(q, k, v, np.zeros(3), lib=lib)
+    np.testing.assert_allclose(o0, v, rtol=1e-13, atol=1e-14)
+    veq = np.broadcast_to(_rng(32).standard_normal(5), v.shape).copy()
+    oe, _ = oracle.fwd_causal_decay(q, k, veq, gam, lib=lib)
+    np.testing.assert_allclose(oe, veq, rtol=1e-12, atol=1e-12)
+    # heads are independent: swapping two heads' gammas swaps their outputs only
+    osw, _ = oracle.fwd_causal_decay(q[:, [1, 0, 2]], k[:, [1, 0, 2]], v[:, [1, 0, 2]], gam[[1, 0, 2]], lib=lib)
+    np.testing.assert_allclose(osw, o[:, [1, 0, 2]], rtol=1e-14, atol=1e-15)
+    S = np.zeros((2, 3, 8, 5))
+    z = np.zeros((2, 3, 8))
+    outs = []
+    for t in range(40):
+        S, z, ot = oracle.decode_step_decay(S, z, q[:, :, t], k[:, :, t], v[:, :, t], gam, lib=lib)
+        outs.append(ot)
+    np.testing.assert_allclose(np.stack(outs, 2), o, rtol=1e-13, atol=1e-14)
+    fk = forms.phi(k)
+    w = gam.reshape(1, 3, 1) ** np.arange(39, -1, -1).reshape(1, 1, 40)
+    np.testing.assert_allclose(z, (fk * w[..., None]).sum(2), rtol=1e-12)
+
+
 ALL_CHECKS = [check_golden, check_causal_vs_quadratic, check_causal_vs_chunked, check_noncausal,
-              check_invariants, check_decode, check_backward, check_backward_noncausal]
+              check_invariants, check_decode, check_backward, check_backward_noncausal, check_decay]
 
 
 def failing_checks(lib):

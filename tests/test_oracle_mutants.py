@@ -60,6 +60,13 @@ MUTANTS = {
                       "for (int e = 0; e < dk; ++e) acc += Sp[(long)e * dv1 + c] * phi(qb[(long)j * dk + e]);"),
     "bwd_dq_missing_chain_rule": ("dqb[(long)i * dk + e] = acc * dphi(qb[(long)i * dk + e]);",
                                   "dqb[(long)i * dk + e] = acc;"),
+    "decay_misses_z": ("z[e] = g * z[e] + fk;", "z[e] = z[e] + fk;"),
+    "decay_after_update": ("S[(long)e * dv + c] = g * S[(long)e * dv + c] + fk * vi[c];",
+                           "S[(long)e * dv + c] = g * (S[(long)e * dv + c] + fk * vi[c]);"),
+    "decay_gamma_by_batch": ("const double g = gamma[bh % H];\n        const double *qb = q + bh * (long)N * dk;",
+                             "const double g = gamma[(bh / H) % H];\n        const double *qb = q + bh * (long)N * dk;"),
+    "decode_decay_misses_S": ("Sb[(long)e * dv + c] = g * Sb[(long)e * dv + c] + fk * vb[c];",
+                              "Sb[(long)e * dv + c] = Sb[(long)e * dv + c] + fk * vb[c];"),
     "nbwd_eps_sign": ("Gi[dv] = -go / d;", "Gi[dv] = go / d;"),
     "nbwd_drops_ones_column": ("double acc = Rp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */",
                                "double acc = 0.0;"),
