@@ -121,6 +121,26 @@ la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void 
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Causal forward with a fixed per-head decay (itwiki "선형 어텐션", table of
+ * later variants, RetNet row, S_t = gamma S_{t-1} + ...), keeping the feature
+ * map and the normaliser of the base method:
+ *   S_i = gamma_h S_{i-1} + phi(k_i) v_i^T,  z_i = gamma_h z_{i-1} + phi(k_i),
+ *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
+ * gamma: device pointer to H fp32 values, gamma_h for head h, each in
+ * [0.25, 1] (the chunked evaluation folds gamma^(+-(C/2 + 1)) into its
+ * operands; smaller values leave the fp32 range).  A NULL gamma is no decay
+ * (la_fwd_causal_state).  S0, z0 enter decayed like any earlier state; S_out,
+ * z_out receive the decayed state after the last token and seed
+ * la_decode_step_decay.  Other arguments, the workspace (the query of
+ * la_fwd_causal) and errors as la_fwd_causal_state.
+ */
+la_status la_fwd_causal_decay(const void *q, const void *k, const void *v, void *o, float *den,
+                              const float *S0, const float *z0, float *S_out, float *z_out, const float *gamma,
+                              int B, int H, int N, int d_k, int d_v, int C,
+                              la_dtype in, la_dtype out,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Causal backward by cumulative sums: the exact gradient of la_fwd_causal
  * with respect to q, k and v for an upstream gradient dO.
  * With g_i = dO_i, den_i = phi(q_i) . z_i, gh_i = g_i / den_i and
@@ -170,6 +190,19 @@ la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const vo
 la_status la_decode_step(float *S, float *z, const void *q, const void *k, const void *v,
                          void *o, int B, int H, int d_k, int d_v, la_dtype in,
                          hipStream_t stream);
+
+/*
+ * Decode step with a fixed per-head decay (itwiki "선형 어텐션", table of
+ * later variants, RetNet row, S_t = gamma S_{t-1} + ...; the feature map and
+ * the normaliser of the base method are kept):
+ *   S = gamma_h S + phi(k) v^T;  z = gamma_h z + phi(k);  o = phi(q)^T S / (phi(q) . z)
+ * gamma: device pointer to H fp32 values, gamma_h for head h (values in
+ * [0, 1]; 1 gives la_decode_step).  Other arguments as la_decode_step; a
+ * NULL gamma returns LA_ERR_NULL_PTR.
+ */
+la_status la_decode_step_decay(float *S, float *z, const void *q, const void *k, const void *v,
+                               void *o, const float *gamma, int B, int H, int d_k, int d_v, la_dtype in,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

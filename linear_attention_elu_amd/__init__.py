@@ -12,8 +12,10 @@ from .binding import (  # noqa: F401
     la_bwd_noncausal_workspace_bytes,
     la_fwd_causal,
     la_fwd_causal_state,
+    la_fwd_causal_decay,
     la_fwd_noncausal,
     la_bwd_causal,
     la_bwd_noncausal,
     la_decode_step,
+    la_decode_step_decay,
 )

@@ -27,9 +27,11 @@ EXPORTS = (
     "la_fwd_noncausal",
     "la_fwd_causal",
     "la_fwd_causal_state",
+    "la_fwd_causal_decay",
     "la_bwd_causal",
     "la_bwd_noncausal",
     "la_decode_step",
+    "la_decode_step_decay",
 )
 
 _lib = None
@@ -68,6 +70,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_fwd_causal.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_fwd_causal.restype = i
     lib.la_fwd_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.la_fwd_causal_decay.argtypes = [vp] * 10 + [i] * 8 + [vp, sz, vp]
+    lib.la_fwd_causal_decay.restype = i
     lib.la_fwd_causal_state.restype = i
     lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_causal.restype = i
@@ -76,6 +80,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_bwd_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_noncausal.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.la_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.la_decode_step_decay.restype = i
     lib.la_decode_step.restype = i
     if path is None:
         _lib = lib

@@ -113,6 +113,33 @@ def la_fwd_causal_state(q, k, v, o=None, den=None, S0=None, z0=None, S_out=None,
     return o, den
 
 
+def la_fwd_causal_decay(q, k, v, gamma, o=None, den=None, S0=None, z0=None, S_out=None, z_out=None,
+                        C: int = 64, out_dtype=None, ws=None, stream=None, want_den: bool = True):
+    """Causal forward with a fixed decay gamma[h] per head (float32 [H] on the
+    device, values in [0.25, 1]) and an optional carried state.  Returns (o, den)."""
+    B, H, N, dk, dv = _shapes(q, k, v)
+    dev = _dev(q, k, v, o, den, S0, z0, S_out, z_out, ws)
+    _gamma(gamma, H, dev)
+    if o is None:
+        o = torch.empty((B, H, N, dv), dtype=out_dtype or q.dtype, device=dev)
+    if den is None and want_den:
+        den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    for t, shp in ((o, (B, H, N, dv)), (den, (B, H, N)), (S0, (B, H, dk, dv)), (z0, (B, H, dk)),
+                   (S_out, (B, H, dk, dv)), (z_out, (B, H, dk))):
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"expected shape {shp}, got {tuple(t.shape)}")
+    for t in (den, S0, z0, S_out, z_out):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("den, S and z are float32")
+    _dev(o, den)
+    wp, wb = _ws(la_fwd_causal_workspace_bytes(B, H, N, dk, dv, C), dev, ws)
+    rc = _lib.load().la_fwd_causal_decay(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(gamma),
+        B, H, N, dk, dv, C, _code(q), _code(o), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_fwd_causal_decay")
+    return o, den
+
+
 def la_fwd_causal(q, k, v, o=None, den=None, C: int = 64, out_dtype=None, ws=None, stream=None,
                   want_den: bool = True):
     """Causal forward.  Returns (o, den) (den is None when want_den is False and none is given)."""
@@ -208,4 +235,37 @@ def la_decode_step(S, z, q, k, v, o=None, stream=None):
     rc = _lib.load().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, dk, dvv,
                                     _code(q), _stream(dev, stream))
     _lib.check(rc, "la_decode_step")
+    return o
+
+
+def _gamma(gamma, H, dev):
+    if not isinstance(gamma, torch.Tensor) or gamma.dtype != torch.float32 or tuple(gamma.shape) != (H,) \
+            or not gamma.is_contiguous():
+        raise ValueError(f"gamma must be a contiguous float32 tensor of shape ({H},)")
+    _dev(gamma)
+    if gamma.device != dev:
+        raise ValueError("gamma must be on the device of the other tensors")
+    return gamma
+
+
+def la_decode_step_decay(S, z, q, k, v, gamma, o=None, stream=None):
+    """One decode step with a fixed decay gamma[h] per head, updating S and z in
+    place.  Returns o [B,H,d_v]."""
+    if S.dim() != 4 or z.dim() != 3 or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,d_k,d_v] and z float32 [B,H,d_k]")
+    B, H, dk, dvv = S.shape
+    if tuple(z.shape) != (B, H, dk) or tuple(q.shape) != (B, H, dk) or tuple(k.shape) != (B, H, dk) \
+            or tuple(v.shape) != (B, H, dvv):
+        raise ValueError("q, k must be [B,H,d_k] and v [B,H,d_v]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    dev = _dev(S, z, q, k, v, o)
+    _gamma(gamma, H, dev)
+    if o is None:
+        o = torch.empty((B, H, dvv), dtype=q.dtype, device=dev)
+    if tuple(o.shape) != (B, H, dvv) or o.dtype != q.dtype:
+        raise ValueError("o must be [B,H,d_v] in the dtype of q")
+    rc = _lib.load().la_decode_step_decay(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(gamma),
+                                          B, H, dk, dvv, _code(q), _stream(dev, stream))
+    _lib.check(rc, "la_decode_step_decay")
     return o

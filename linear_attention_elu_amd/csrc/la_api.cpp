@@ -121,8 +121,8 @@ size_t la_bwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v) {
     return la::bwd_workspace_bytes(B, H, N, d_k, d_v, kNonCausalChunk);
 }
 
-la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void *o, float *den,
-                              const float *S0, const float *z0, float *S_out, float *z_out,
+la_status la_fwd_causal_decay(const void *q, const void *k, const void *v, void *o, float *den,
+                              const float *S0, const float *z0, float *S_out, float *z_out, const float *gamma,
                               int B, int H, int N, int d_k, int d_v, int C,
                               la_dtype in, la_dtype out,
                               void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -140,8 +140,17 @@ la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void 
     const size_t need = fwd_ws_bytes(B, H, N, d_k, d_v, C, true);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
     la::FwdDesc d{q, k, v, o, den, S0, z0, S_out, z_out, B, H, N, d_k, d_v, C,
-                  in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream};
+                  in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream, gamma};
     return run_fwd(d, true);
+}
+
+la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void *o, float *den,
+                              const float *S0, const float *z0, float *S_out, float *z_out,
+                              int B, int H, int N, int d_k, int d_v, int C,
+                              la_dtype in, la_dtype out,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+    return la_fwd_causal_decay(q, k, v, o, den, S0, z0, S_out, z_out, nullptr, B, H, N, d_k, d_v, C, in, out,
+                               ws, ws_bytes, stream);
 }
 
 la_status la_fwd_causal(const void *q, const void *k, const void *v, void *o, float *den,
@@ -165,7 +174,7 @@ la_status la_fwd_noncausal(const void *q, const void *k, const void *v, void *o,
     const size_t need = fwd_ws_bytes(B, H, N, d_k, d_v, kNonCausalChunk, false);
     if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
     la::FwdDesc d{q, k, v, o, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, N, d_k, d_v, kNonCausalChunk,
-                  in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream};
+                  in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream, nullptr};
     return run_fwd(d, false);
 }
 
@@ -215,7 +224,21 @@ la_status la_decode_step(float *S, float *z, const void *q, const void *k, const
     if (!dtype_ok(in)) return LA_ERR_BAD_DTYPE;
     if (!aligned(S) || !aligned(z) || !aligned(q) || !aligned(k) || !aligned(v) || !aligned(o))
         return LA_ERR_ALIGNMENT;
-    la::DecodeDesc d{S, z, q, k, v, o, B, H, d_k, d_v, in == LA_BF16, stream};
+    la::DecodeDesc d{S, z, q, k, v, o, B, H, d_k, d_v, in == LA_BF16, stream, nullptr};
+    return from_hip(la::run_decode(d));
+}
+
+la_status la_decode_step_decay(float *S, float *z, const void *q, const void *k, const void *v,
+                               void *o, const float *gamma, int B, int H, int d_k, int d_v, la_dtype in,
+                               hipStream_t stream) {
+    if (!S || !z || !q || !k || !v || !o || !gamma) return LA_ERR_NULL_PTR;
+    la_status st = check_shape(B, H, 1);
+    if (st != LA_OK) return st;
+    if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in)) return LA_ERR_BAD_DTYPE;
+    if (!aligned(S) || !aligned(z) || !aligned(q) || !aligned(k) || !aligned(v) || !aligned(o))
+        return LA_ERR_ALIGNMENT;
+    la::DecodeDesc d{S, z, q, k, v, o, B, H, d_k, d_v, in == LA_BF16, stream, gamma};
     return from_hip(la::run_decode(d));
 }
 

@@ -12,6 +12,10 @@
 // row) and 64 / (d_v / 4) rows at a time, so each wave-wide access is one
 // contiguous block of S.  Column sums of phi(q) * S are reduced across the
 // rows a wave holds with lane shuffles; phi(q) . z across the wave.
+//
+// With a per-head decay (itwiki "선형 어텐션", table of later variants, RetNet
+// row) the update is S = gamma_h S + phi(k) v^T, z = gamma_h z + phi(k); a
+// null gamma is gamma = 1, the plain step.
 #include "la_device.hpp"
 #include "la_internal.h"
 
@@ -20,13 +24,15 @@ namespace la {
 template <int DK, int DV, typename TI>
 __global__ void __launch_bounds__(256)
 la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__restrict__ q,
-                 const void *__restrict__ k, const void *__restrict__ v, void *__restrict__ o, long BH) {
+                 const void *__restrict__ k, const void *__restrict__ v, void *__restrict__ o, long BH,
+                 const float *__restrict__ gamma, int H) {
     constexpr int CV = DV / 4;   // lanes per row of S (one float4 each)
     constexpr int RG = 64 / CV;  // rows of S a wave covers per access
     constexpr int RPL = DK / RG; // accesses per lane
     const int lane = threadIdx.x & 63;
     const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (bh >= BH) return;  // whole waves leave; no block-wide barrier follows
+    const float gm = gamma ? gamma[bh % H] : 1.0f;
 
     const int cg = lane % CV;
     const int r0 = lane / CV;
@@ -55,7 +61,7 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
             f32x4 s = sreg[t];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                s[c] = s[c] + fk * vv[c];
+                s[c] = gm * s[c] + fk * vv[c];
                 num[c] += fq * s[c];
             }
             *reinterpret_cast<f32x4 *>(Sb + (long)e * DV + 4 * cg) = s;
@@ -72,7 +78,7 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
     for (int h = 0; h < (DK + 63) / 64; ++h) {
         const int e = lane + 64 * h;
         if (e < DK) {
-            const float zn = z[qk0 + e] + phi(Store<TI>::load(k, qk0 + e));
+            const float zn = gm * z[qk0 + e] + phi(Store<TI>::load(k, qk0 + e));
             z[qk0 + e] = zn;
             dpart += phi(Store<TI>::load(q, qk0 + e)) * zn;
         }
@@ -99,9 +105,9 @@ static hipError_t run_decode_t(const DecodeDesc &d) {
     const long BH = (long)d.B * d.H;
     const dim3 grid((unsigned)((BH + 3) / 4));
     if (d.in_bf16)
-        la_decode_kernel<DK, DV, __bf16><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH);
+        la_decode_kernel<DK, DV, __bf16><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH, d.gamma, d.H);
     else
-        la_decode_kernel<DK, DV, float><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH);
+        la_decode_kernel<DK, DV, float><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH, d.gamma, d.H);
     return hipGetLastError();
 }
 

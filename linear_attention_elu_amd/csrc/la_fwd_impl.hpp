@@ -86,6 +86,8 @@ struct FwdParams {
     int state_P;            // segments per (bh) in the state array
     int state_mult;         // segment s of this launch starts at state slot s * state_mult
     int seg_base;           // segment of workgroup row blockIdx.y: seg_base + blockIdx.y
+    const float *gamma;     // MODE_CAUSAL, MODE_AGG: per-head decay [H], or null for none
+    int H;                  // heads (bh % H is the head of workgroup column bh)
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -131,6 +133,16 @@ __device__ LA_INLINE void static_for_impl(F &&f, std::integer_sequence<int, Is..
 }
 template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// g^n for an integer n (of either sign) by repeated squaring in fp32.
+__device__ __forceinline__ float powi(float g, int n) {
+    float r = 1.0f, b = g;
+    for (int e = n < 0 ? -n : n; e > 0; e >>= 1) {
+        if (e & 1) r *= b;
+        b *= b;
+    }
+    return n < 0 ? 1.0f / r : r;
 }
 
 // OBF: the output o is bf16 (else fp32).
@@ -184,6 +196,17 @@ la_chunk_kernel(const FwdParams p) {
     const int pp = lane & 15;
     const long bh = blockIdx.x;
     const int seg = p.seg_base + (int)blockIdx.y;
+    // Per-head decay gamma (RetNet row of the itwiki variants table), folded into
+    // the operands: with tau the row inside a chunk and m = CT / 2, phi(q) rows
+    // are staged times gamma^(tau - m) and phi(k) rows times gamma^(m - tau), so
+    // every in-chunk score carries gamma^(tau_i - tau_j); the carried state is
+    // read as gamma^(m + 1) S, and a chunk of R rows updates it to
+    // gamma^(R - 1 - m) (gamma^(m + 1) S + sum phi~(k) v^T).  The factors stay
+    // within 2^(+-(m + 1) log2(1 / gamma)), in range for gamma >= 1/4.
+    const bool decay = (MODE == MODE_CAUSAL || MODE == MODE_AGG) && p.gamma != nullptr;
+    const float gam = decay ? p.gamma[bh % p.H] : 1.0f;
+    constexpr int DM = CT / 2;
+    const float g_in = decay ? powi(gam, DM + 1) : 1.0f;
     const int N = p.N;
     const int row_begin = seg * p.L;
     const int row_end = min(N, row_begin + p.L);
@@ -283,12 +306,19 @@ la_chunk_kernel(const FwdParams p) {
         auto load_any = [&](auto set_tag, int c) LA_INLINE { load(set_tag, Part{}, c); };
 
         // phi (times a factor) of a 16-byte vector of inputs, as a 16-byte vector of TC.
+        // decay factors of this thread's q and k vectors (rows rq0 + i RSQ of every chunk)
+        float qdec[NLQ], kdec[NLQ];
+#pragma unroll
+        for (int i = 0; i < NLQ; ++i) {
+            qdec[i] = decay ? powi(gam, rq0 + i * RSQ - DM) : 1.0f;
+            kdec[i] = decay ? powi(gam, DM - rq0 - i * RSQ) : 1.0f;
+        }
         auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
             float x[VEC];
             unpack16(u, x, TI());
             Frag<TC> w;
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) w.set(t, WEIGHTED ? phi(x[t]) * scale : phi(x[t]));
+            for (int t = 0; t < VEC; ++t) w.set(t, phi(x[t]) * scale);
             if constexpr (sizeof(TC) == 2) {
                 return __builtin_bit_cast(uint4, w.v);
             } else {
@@ -308,7 +338,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rq[S][i], 1.0f);
+                        uint4 out = phi16(rq[S][i], qdec[i]);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_Q + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -318,7 +348,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : 1.0f);
+                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : kdec[i]);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -426,14 +456,16 @@ la_chunk_kernel(const FwdParams p) {
     // all sixteen operand rows are the same vector).
     Frag<TC> fragS[CBW][NSE];
     Frag<TC> fragZ[NSE];
+    // (with decay the operands hold gamma^(m + 1) S and gamma^(m + 1) z; g_in = 1 otherwise)
     auto refresh_state_frags = [&]() LA_INLINE {
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NSE; ++s) {
 #pragma unroll
             for (int cs = 0; cs < CBW; ++cs)
-                acc_to_frag(fragS[cs][s], accS[cs][2 * s], (2 * s + 1 < NE) ? accS[cs][2 * s + 1] : zero4);
-            acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
+                acc_to_frag(fragS[cs][s], accS[cs][2 * s] * g_in,
+                            (2 * s + 1 < NE) ? accS[cs][2 * s + 1] * g_in : zero4);
+            acc_to_frag(fragZ[s], accZ[2 * s] * g_in, (2 * s + 1 < NE) ? accZ[2 * s + 1] * g_in : zero4);
         }
     };
     if (!AGGM) refresh_state_frags();
@@ -641,7 +673,7 @@ la_chunk_kernel(const FwdParams p) {
     // Compute the chunk in LDS buffer b: outputs into outv/den, `store(I)`
     // writes row block I as soon as it is done and `store(-1)` the den, then
     // the state carry.
-    auto compute = [&](int b, auto &&store) LA_INLINE {
+    auto compute = [&](int b, int crows, auto &&store) LA_INLINE {
         const char *buf = smem + b * T::BUF;
         const int qoff = (b * T::BUF + T::OFF_Q) / (int)sizeof(TC);  // tile offsets in elements
         const int koff = (b * T::BUF + T::OFF_K) / (int)sizeof(TC);
@@ -657,6 +689,14 @@ la_chunk_kernel(const FwdParams p) {
         store(-1, outv, den);
 
         // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
+        if (NEED_K && has_cols && decay) {
+#pragma unroll
+            for (int E = 0; E < NE; ++E) {
+                accZ[E] = accZ[E] * g_in;
+#pragma unroll
+                for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_in;
+            }
+        }
         if (NEED_K && has_cols) {
             const float *sw = reinterpret_cast<const float *>(buf + T::OFF_W);
 #pragma unroll
@@ -690,6 +730,15 @@ la_chunk_kernel(const FwdParams p) {
                     }
                 }
                     }
+            if (decay) {
+                const float g_out = powi(gam, crows - 1 - DM);
+#pragma unroll
+                for (int E = 0; E < NE; ++E) {
+                    accZ[E] = accZ[E] * g_out;
+#pragma unroll
+                    for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_out;
+                }
+            }
             if (MODE == MODE_CAUSAL) refresh_state_frags();
         }
     };
@@ -702,16 +751,16 @@ la_chunk_kernel(const FwdParams p) {
         if constexpr (NBUF == 2) {
             for (; j + 3 < nfull; j += 2) {  // same trip count as the staging waves
                 __syncthreads();
-                compute(0, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
+                compute(0, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
                 __syncthreads();
-                compute(1, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j + 1, CT, part, o, d); });
+                compute(1, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j + 1, CT, part, o, d); });
             }
         }
         for (; j < nch; ++j) {
             const int b = NBUF == 2 ? (j & 1) : 0;
             __syncthreads();
-            if (j < nfull) compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
-            else compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, j, rows_of(j), part, o, d); });
+            if (j < nfull) compute(b, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
+            else compute(b, rows_of(j), [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, j, rows_of(j), part, o, d); });
             if (NBUF == 1 && j + 1 < nch) __syncthreads();  // the staging waves refill the single buffer
         }
     } else {
@@ -728,12 +777,12 @@ la_chunk_kernel(const FwdParams p) {
                 const int b = ch & 1;
                 stage(S0t{}, Full{}, b ^ 1, CT);
                 load(S0t{}, Full{}, ch + 2);
-                compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+                compute(b, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
                 __syncthreads();
             }
         } else {
             for (; ch + 2 < nfull; ++ch) {
-                compute(0, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+                compute(0, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
                 __syncthreads();
                 stage(S0t{}, Full{}, 0, CT);
                 load(S0t{}, Full{}, ch + 2);
@@ -747,8 +796,8 @@ la_chunk_kernel(const FwdParams p) {
                 else stage(S0t{}, Part{}, b ^ 1, rows_of(ch + 1));
                 if (ch + 2 < nch) load_any(S0t{}, ch + 2);
             }
-            if (ch < nfull) compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
-            else compute(b, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, ch, rows_of(ch), part, o, d); });
+            if (ch < nfull) compute(b, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+            else compute(b, rows_of(ch), [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, ch, rows_of(ch), part, o, d); });
             __syncthreads();
             if (NBUF == 1 && ch + 1 < nch) {
                 if (ch + 1 < nfull) stage(S0t{}, Full{}, 0, CT);

@@ -48,6 +48,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     if (causal) {
         p.S_fin = d.S_out;
         p.z_fin = d.z_out;
+        p.gamma = d.gamma;
+        p.H = d.H;
         if (Pm > 1) {
             // Only the segments before the last one need their sums: the
             // last causal segment starts at fine slot (Pm - 1) * mult.
@@ -57,7 +59,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
             p.state_mult = 1;
             agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
-            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, nagg, d.stream)) != hipSuccess)
+            if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
+                hipSuccess)
                 return err;
             p.seg_state = d.ws;
             p.state_mult = mult;

@@ -19,6 +19,7 @@ struct FwdDesc {
     int in_bf16, out_bf16;
     float *ws;
     hipStream_t stream;
+    const float *gamma;  // causal only: per-head decay [H] (device), or null for none
 };
 
 struct DecodeDesc {
@@ -28,6 +29,7 @@ struct DecodeDesc {
     int B, H, DK, DV;
     int in_bf16;
     hipStream_t stream;
+    const float *gamma;  // per-head decay [H] (device), or null for none
 };
 
 struct BwdDesc {
@@ -68,8 +70,11 @@ inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 // mode 1 writes the total of all P slots into slot 0; mode 2 replaces slots
 // [lim, P) by their exclusive suffix and writes the sum of all of them into
 // slot lim - 1 (when lim > 0).  Other slots are not touched.  Fixed order.
+// With gamma non-null (mode 0), the segments hold L tokens each and decay by
+// gamma[bh % H] per token: entering(s) = gamma^L entering(s - 1) + aggregate(s - 1).
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
-                           int mode, int lim, hipStream_t stream);
+                           int mode, int lim, hipStream_t stream, const float *gamma = nullptr, int H = 1,
+                           int L = 0);
 
 hipError_t run_fwd_dk16(const FwdDesc &d, bool causal);
 hipError_t run_fwd_dk32(const FwdDesc &d, bool causal);

@@ -20,14 +20,26 @@ namespace la {
 //           [max(lim - 1, 0), P) are written.
 // Slots outside those ranges are neither read nor written, so a caller
 // aggregates only the segments whose sums some later pass reads.
+// With a per-head decay (gamma non-null, mode 0) every segment holds L
+// tokens and its aggregate is taken at its last token, so the state entering
+// segment s is gamma^L times the state entering s - 1 plus the aggregate of s - 1.
 static __global__ void __launch_bounds__(256)
-la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode, int lim) {
+la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode, int lim,
+                   const float *gamma, int H, int L) {
     const int SS = DK * DV + DK;
     const long bh = blockIdx.x;
     const int idx = blockIdx.y * 256 + threadIdx.x;
     if (idx >= SS) return;
     float *base = ws + bh * (long)P * SS + idx;
     if (mode == 0) {
+        float f = 1.0f;  // gamma^L by repeated squaring
+        if (gamma) {
+            float b = gamma[bh % H];
+            for (int e = L; e > 0; e >>= 1) {
+                if (e & 1) f *= b;
+                b *= b;
+            }
+        }
         float run = 0.f;
         if (idx < DK * DV) {
             if (S0) run = S0[bh * (long)DK * DV + idx];
@@ -37,7 +49,7 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
         for (int s = 0; s < lim; ++s) {
             const float a = base[(long)s * SS];
             base[(long)s * SS] = run;
-            run += a;
+            run = f * run + a;
         }
         if (lim < P) base[(long)lim * SS] = run;
     } else if (mode == 1) {
@@ -56,11 +68,11 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
 }
 
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
-                           int mode, int lim, hipStream_t stream) {
+                           int mode, int lim, hipStream_t stream, const float *gamma, int H, int L) {
     if (lim < 0 || lim > P) return hipErrorInvalidValue;
     const long SS = state_floats(DK, DV);
     const dim3 grid((unsigned)BH, (unsigned)((SS + 255) / 256));
-    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode, lim);
+    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode, lim, gamma, H, L);
     return hipGetLastError();
 }
 

@@ -160,6 +160,36 @@ def test_bwd_noncausal_rejects(lib):
     assert f(*bad) == 5
 
 
+def test_fwd_causal_decay_rejects(lib):
+    f = lib.la_fwd_causal_decay
+    need = la.la_fwd_causal_workspace_bytes(1, 1, 64, 64, 64, 64)
+    args = [P] * 4 + [None] * 5 + [P] + [1, 1, 64, 64, 64, 64, 1, 1, P, max(need, 16), None]
+    bad = list(args)
+    bad[5] = P  # S0 without z0
+    assert f(*bad) == 1
+    bad = list(args)
+    bad[13] = 48  # d_k
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[15] = 8  # C
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[17] = 2  # out dtype
+    assert f(*bad) == 4
+    bad = list(args)
+    bad[2] = MIS  # v
+    assert f(*bad) == 7
+
+
+def test_decode_decay_rejects(lib):
+    f = lib.la_decode_step_decay
+    assert f(P, P, P, P, P, P, None, 1, 1, 32, 32, 0, None) == 1
+    assert f(P, P, P, P, P, P, P, 0, 1, 32, 32, 0, None) == 2
+    assert f(P, P, P, P, P, P, P, 1, 1, 8, 32, 0, None) == 3
+    assert f(P, P, P, P, P, P, P, 1, 1, 32, 32, 7, None) == 4
+    assert f(P, MIS, P, P, P, P, P, 1, 1, 32, 32, 0, None) == 7
+
+
 def test_decode_rejects(lib):
     f = lib.la_decode_step
     assert f(None, P, P, P, P, P, 1, 1, 32, 32, 0, None) == 1

@@ -1,0 +1,139 @@
+"""Parity of the per-head decay variant (forward and decode) with the fp64
+oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_elu_amd as la
+import oracle
+from gpu_util import announce, assert_close, device_inputs, need_gpu, row_rel_l2, to64
+
+pytestmark = pytest.mark.gpu
+
+DECAY_CASES = [
+    (2, 2, 64, 16, 32, 16),
+    (2, 3, 50, 16, 32, 16),     # ragged last chunk
+    (1, 1, 1, 64, 64, 64),      # a single token
+    (1, 4, 300, 64, 64, 64),
+    (1, 2, 777, 32, 64, 32),
+    (1, 2, 129, 128, 32, 16),
+    (1, 2, 700, 128, 128, 64),
+    (2, 2, 5000, 64, 64, 64),   # several segments per (batch, head): the scan decays too
+    (1, 3, 3001, 64, 32, 32),
+]
+
+
+def gammas(H, dev):
+    """Per-head decays spanning the supported range [0.25, 1]."""
+    g = np.array([0.25, 0.9, 0.995, 1.0, 0.5, 0.99][:H] if H <= 6 else np.linspace(0.25, 1.0, H))
+    return g, torch.tensor(g, dtype=torch.float32, device=dev)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", DECAY_CASES, ids=lambda c: "B{}_H{}_N{}_dk{}_dv{}_C{}".format(*c))
+def test_decay_forward_matches_oracle(case, dtype):
+    dev = need_gpu()
+    B, H, N, dk, dv, C = case
+    announce(f"decay fwd {dtype} {case}")
+    x, x64 = device_inputs(B, H, N, dk, dv, dtype, seed=sum(case) + 3)
+    g64, g = gammas(H, dev)
+    o, den = la.la_fwd_causal_decay(x["q"], x["k"], x["v"], g, C=C)
+    torch.cuda.synchronize(dev)
+    # the oracle takes gamma as the fp32 value the kernel reads
+    ref, dref = oracle.fwd_causal_decay(x64["q"], x64["k"], x64["v"], g.cpu().double().numpy())
+    assert_close(to64(o), ref, dtype, "out")
+    rel = np.abs(to64(den) - dref) / dref
+    assert rel.max() <= (1e-5 if dtype == "f32" else 2e-2), rel.max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_one_is_the_causal_form(dtype):
+    """gamma = 1 for every head gives the plain causal forward, bit for bit."""
+    dev = need_gpu()
+    x, _ = device_inputs(2, 3, 2500, 64, 64, dtype, seed=5, exact=False)
+    g = torch.ones(3, dtype=torch.float32, device=dev)
+    o1, d1 = la.la_fwd_causal_decay(x["q"], x["k"], x["v"], g, C=64)
+    o2, d2 = la.la_fwd_causal(x["q"], x["k"], x["v"], C=64)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(o1, o2) and torch.equal(d1, d2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_state_handoff(dtype):
+    """Two decayed calls over the halves of a sequence, the second seeded with
+    the first's final state, match the oracle over the whole sequence."""
+    dev = need_gpu()
+    B, H, N, dk, dv = 2, 2, 1000, 64, 32
+    x, x64 = device_inputs(B, H, N, dk, dv, dtype, seed=8)
+    _, g = gammas(H, dev)
+    h = 448
+    S = torch.empty(B, H, dk, dv, device=dev)
+    z = torch.empty(B, H, dk, device=dev)
+    first = [t[:, :, :h].contiguous() for t in (x["q"], x["k"], x["v"])]
+    second = [t[:, :, h:].contiguous() for t in (x["q"], x["k"], x["v"])]
+    o1, _ = la.la_fwd_causal_decay(*first, g, S_out=S, z_out=z, C=64)
+    o2, _ = la.la_fwd_causal_decay(*second, g, S0=S, z0=z, S_out=S, z_out=z, C=64)
+    torch.cuda.synchronize(dev)
+    ref, _ = oracle.fwd_causal_decay(x64["q"], x64["k"], x64["v"], g.cpu().double().numpy())
+    assert_close(np.concatenate([to64(o1), to64(o2)], axis=2), ref, dtype, "out")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_decode_steps_match_oracle(dtype):
+    dev = need_gpu()
+    B, H, T, dk, dv = 3, 4, 40, 32, 64
+    x, x64 = device_inputs(B, H, T, dk, dv, dtype, seed=11)
+    _, g = gammas(H, dev)
+    g64 = g.cpu().double().numpy()
+    S = torch.zeros(B, H, dk, dv, device=dev)
+    z = torch.zeros(B, H, dk, device=dev)
+    So = np.zeros((B, H, dk, dv))
+    zo = np.zeros((B, H, dk))
+    for t in range(T):
+        qt, kt, vt = (x[n][:, :, t].contiguous() for n in ("q", "k", "v"))
+        o = la.la_decode_step_decay(S, z, qt, kt, vt, g)
+        So, zo, oo = oracle.decode_step_decay(So, zo, x64["q"][:, :, t], x64["k"][:, :, t], x64["v"][:, :, t], g64)
+        torch.cuda.synchronize(dev)
+        assert_close(to64(o), oo, dtype, f"step {t}")
+    assert np.abs(to64(S) - So).max() / np.abs(So).max() < 1e-5
+    np.testing.assert_allclose(to64(z), zo, rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decay_prefill_then_decode(dtype):
+    """A decayed prefill hands its final state to decayed decode steps; the
+    outputs of both match the oracle's forward over the whole sequence."""
+    dev = need_gpu()
+    B, H, N, T, dk, dv = 2, 3, 500, 24, 64, 64
+    x, x64 = device_inputs(B, H, N + T, dk, dv, dtype, seed=13)
+    _, g = gammas(H, dev)
+    S = torch.empty(B, H, dk, dv, device=dev)
+    z = torch.empty(B, H, dk, device=dev)
+    pre = [t[:, :, :N].contiguous() for t in (x["q"], x["k"], x["v"])]
+    o_pre, _ = la.la_fwd_causal_decay(*pre, g, S_out=S, z_out=z, C=64)
+    outs = [la.la_decode_step_decay(S, z, *(x[n][:, :, N + t].contiguous() for n in ("q", "k", "v")), g)
+            for t in range(T)]
+    torch.cuda.synchronize(dev)
+    ref, _ = oracle.fwd_causal_decay(x64["q"], x64["k"], x64["v"], g.cpu().double().numpy())
+    assert_close(to64(o_pre), ref[:, :, :N], dtype, "prefill")
+    assert_close(to64(torch.stack(outs, 2)), ref[:, :, N:], dtype, "decode")
+
+
+def test_decay_workload_sampled():
+    """The headline shape B=8, H=8, N=65536, d=64, C=64, bf16, seed 0, with
+    decays 1 - 2^-(3 + h); every row of three sampled (batch, head) pairs
+    against the oracle."""
+    dev = need_gpu()
+    B, H, N, d = 8, 8, 65536, 64
+    announce("decay workload")
+    x, _ = device_inputs(B, H, N, d, d, "bf16", seed=0, exact=False)
+    g = torch.tensor([1.0 - 2.0 ** -(3 + h) for h in range(H)], dtype=torch.float32, device=dev)
+    o, _ = la.la_fwd_causal_decay(x["q"], x["k"], x["v"], g, C=64, want_den=False)
+    torch.cuda.synchronize(dev)
+    g64 = g.cpu().double().numpy()
+    for (b, h) in [(0, 0), (3, 5), (7, 7)]:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref, _ = oracle.fwd_causal_decay(*(to64(x[n][sl]) for n in ("q", "k", "v")), g64[h:h + 1])
+        err = row_rel_l2(to64(o[sl]), ref)
+        print(f"(b={b}, h={h}) row-wise relative L2 {err:.3e}")
+        assert err <= 2e-2, (b, h, err)
