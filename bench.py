@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="skip the sweep / non-causal / backward lines")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "decay", "copy"], default=None,
                     help="run one leg only (for profiler runs); prints its own JSON line")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the plain copy leg")
     return ap.parse_args()
@@ -121,6 +121,27 @@ def bench_fwd(steps, warmup, dev, B=8, H=8, N=65536, d=64, C=64, seed=0):
         "ms": ms, "tokens_per_s": B * N / (ms * 1e-3), "bytes": bytes_alg, "flops": flops_alg,
         "gbs": bytes_alg / (ms * 1e-3) / 1e9, "tflops": flops_alg / (ms * 1e-3) / 1e12,
     }
+
+
+def bench_fwd_decay(steps, warmup, dev, B=8, H=8, N=65536, d=64, C=64, seed=0):
+    """The headline shape with a fixed decay per head, 1 - 2^-(3 + h)."""
+    import torch
+
+    import linear_attention_elu_amd as la
+    from linear_attention_elu_amd import inputs
+
+    host = inputs.attention_inputs(B, H, N, d, d, seed=seed)
+    q, k, v = (inputs.to_torch(host[n], torch.bfloat16, dev) for n in ("q", "k", "v"))
+    del host
+    g = torch.tensor([1.0 - 2.0 ** -(3 + h) for h in range(H)], dtype=torch.float32, device=dev)
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, la.la_fwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
+    ms = time_calls(lambda: la.la_fwd_causal_decay(q, k, v, g, o=o, C=C, ws=ws, want_den=False), steps, warmup,
+                    torch.cuda.current_stream(dev))
+    by = B * H * N * 4 * d * 2
+    return {"workload": f"causal_decay_fwd_bf16_B{B}_H{H}_N{N}_d{d}_C{C}", "us": round(ms * 1e3, 2),
+            "tokens_per_s": round(B * N / (ms * 1e-3), 1), "achieved_GBs": round(by / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def bench_decode(dev, T=3072, B=256, H=8, d=32, seed=0, reps=5):
@@ -333,6 +354,8 @@ def main():
             r = bench_noncausal(dev, args.steps, args.warmup)
         elif args.only == "bwd":
             r = bench_bwd(dev, args.steps, args.warmup)
+        elif args.only == "decay":
+            r = bench_fwd_decay(args.steps, args.warmup, dev)
         else:
             r = bench_copy(dev, args.copy_mib, args.steps, args.warmup)
         print(json.dumps({"only": args.only, **r}))
@@ -382,7 +405,7 @@ def main():
                              "hbm_frac": round(s["gbs"] / HBM_PEAK_GBS, 4),
                              "mfma_frac": round(s["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
         res["extra"] = {"causal_sweep_B8_H8_d64_C64": sweep, "noncausal": bench_noncausal(dev),
-                        "fwd_bwd": bench_bwd(dev)}
+                        "fwd_bwd": bench_bwd(dev), "causal_decay": bench_fwd_decay(args.steps, args.warmup, dev)}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on host cores")
         res["cpu_baseline"] = cpu_baseline()

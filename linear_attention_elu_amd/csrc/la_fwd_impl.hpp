@@ -145,8 +145,10 @@ __device__ __forceinline__ float powi(float g, int n) {
     return n < 0 ? 1.0f / r : r;
 }
 
-// OBF: the output o is bf16 (else fp32).
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF>
+// OBF: the output o is bf16 (else fp32).  DECAY (MODE_CAUSAL and MODE_AGG):
+// the per-head decay of p.gamma; a separate instantiation, so that the plain
+// kernels keep their registers.
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false>
 __global__ void __launch_bounds__((fwd_threads<DK, DV, TI>()))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE>())))
 la_chunk_kernel(const FwdParams p) {
@@ -203,7 +205,7 @@ la_chunk_kernel(const FwdParams p) {
     // read as gamma^(m + 1) S, and a chunk of R rows updates it to
     // gamma^(R - 1 - m) (gamma^(m + 1) S + sum phi~(k) v^T).  The factors stay
     // within 2^(+-(m + 1) log2(1 / gamma)), in range for gamma >= 1/4.
-    const bool decay = (MODE == MODE_CAUSAL || MODE == MODE_AGG) && p.gamma != nullptr;
+    constexpr bool decay = DECAY && (MODE == MODE_CAUSAL || MODE == MODE_AGG);
     const float gam = decay ? p.gamma[bh % p.H] : 1.0f;
     constexpr int DM = CT / 2;
     const float g_in = decay ? powi(gam, DM + 1) : 1.0f;
@@ -307,18 +309,20 @@ la_chunk_kernel(const FwdParams p) {
 
         // phi (times a factor) of a 16-byte vector of inputs, as a 16-byte vector of TC.
         // decay factors of this thread's q and k vectors (rows rq0 + i RSQ of every chunk)
-        float qdec[NLQ], kdec[NLQ];
+        float qdec[decay ? NLQ : 1], kdec[decay ? NLQ : 1];
 #pragma unroll
         for (int i = 0; i < NLQ; ++i) {
-            qdec[i] = decay ? powi(gam, rq0 + i * RSQ - DM) : 1.0f;
-            kdec[i] = decay ? powi(gam, DM - rq0 - i * RSQ) : 1.0f;
+            if constexpr (decay) {
+                qdec[i] = powi(gam, rq0 + i * RSQ - DM);
+                kdec[i] = powi(gam, DM - rq0 - i * RSQ);
+            }
         }
         auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
             float x[VEC];
             unpack16(u, x, TI());
             Frag<TC> w;
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) w.set(t, phi(x[t]) * scale);
+            for (int t = 0; t < VEC; ++t) w.set(t, (WEIGHTED || decay) ? phi(x[t]) * scale : phi(x[t]));
             if constexpr (sizeof(TC) == 2) {
                 return __builtin_bit_cast(uint4, w.v);
             } else {
@@ -338,7 +342,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rq[S][i], qdec[i]);
+                        uint4 out = phi16(rq[S][i], decay ? qdec[decay ? i : 0] : 1.0f);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_Q + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -348,7 +352,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : kdec[i]);
+                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : (decay ? kdec[decay ? i : 0] : 1.0f));
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -463,9 +467,15 @@ la_chunk_kernel(const FwdParams p) {
         for (int s = 0; s < NSE; ++s) {
 #pragma unroll
             for (int cs = 0; cs < CBW; ++cs)
-                acc_to_frag(fragS[cs][s], accS[cs][2 * s] * g_in,
-                            (2 * s + 1 < NE) ? accS[cs][2 * s + 1] * g_in : zero4);
-            acc_to_frag(fragZ[s], accZ[2 * s] * g_in, (2 * s + 1 < NE) ? accZ[2 * s + 1] * g_in : zero4);
+                if constexpr (decay)
+                    acc_to_frag(fragS[cs][s], accS[cs][2 * s] * g_in,
+                                (2 * s + 1 < NE) ? accS[cs][2 * s + 1] * g_in : zero4);
+                else
+                    acc_to_frag(fragS[cs][s], accS[cs][2 * s], (2 * s + 1 < NE) ? accS[cs][2 * s + 1] : zero4);
+            if constexpr (decay)
+                acc_to_frag(fragZ[s], accZ[2 * s] * g_in, (2 * s + 1 < NE) ? accZ[2 * s + 1] * g_in : zero4);
+            else
+                acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
         }
     };
     if (!AGGM) refresh_state_frags();
@@ -689,12 +699,14 @@ la_chunk_kernel(const FwdParams p) {
         store(-1, outv, den);
 
         // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
-        if (NEED_K && has_cols && decay) {
+        if constexpr (decay) {
+            if (NEED_K && has_cols) {
 #pragma unroll
-            for (int E = 0; E < NE; ++E) {
-                accZ[E] = accZ[E] * g_in;
+                for (int E = 0; E < NE; ++E) {
+                    accZ[E] = accZ[E] * g_in;
 #pragma unroll
-                for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_in;
+                    for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_in;
+                }
             }
         }
         if (NEED_K && has_cols) {
@@ -730,7 +742,7 @@ la_chunk_kernel(const FwdParams p) {
                     }
                 }
                     }
-            if (decay) {
+            if constexpr (decay) {
                 const float g_out = powi(gam, crows - 1 - DM);
 #pragma unroll
                 for (int E = 0; E < NE; ++E) {

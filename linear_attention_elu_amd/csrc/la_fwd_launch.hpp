@@ -11,23 +11,24 @@
 namespace la {
 
 // Resident workgroups of one instantiation of the chunk kernel (cached).
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false>
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool DECAY = false>
 long chunk_resident() {
     static OccCache cache;
-    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF>), cache,
-                               fwd_threads<DK, DV, TI>());
+    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY>),
+                               cache, fwd_threads<DK, DV, TI>());
 }
 
-template <int DK, int DV, typename TI, int CT, bool OBF>
+// DECAY: the causal form with a per-head decay (d.gamma non-null).
+template <int DK, int DV, typename TI, int CT, bool OBF, bool DECAY>
 hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT, false>;
-    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF>
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT, false, DECAY>;
+    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>
                               : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
-    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT>();
-    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF>()
+    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT, false, DECAY>();
+    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>()
                                     : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF>();
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
@@ -103,10 +104,18 @@ template <int DK, int DV, typename TI> constexpr int fwd_chunk(int C) {
 template <int DK, int DV, typename TI>
 hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     const bool obf = d.out_bf16 != 0;
+    const bool dec = causal && d.gamma != nullptr;
+    auto pick = [&](auto ct) {
+        constexpr int CT = decltype(ct)::value;
+        if (dec) return obf ? run_fwd_ct<DK, DV, TI, CT, true, true>(d, causal)
+                            : run_fwd_ct<DK, DV, TI, CT, false, true>(d, causal);
+        return obf ? run_fwd_ct<DK, DV, TI, CT, true, false>(d, causal)
+                   : run_fwd_ct<DK, DV, TI, CT, false, false>(d, causal);
+    };
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
-        case 16: return obf ? run_fwd_ct<DK, DV, TI, 16, true>(d, causal) : run_fwd_ct<DK, DV, TI, 16, false>(d, causal);
-        case 32: return obf ? run_fwd_ct<DK, DV, TI, 32, true>(d, causal) : run_fwd_ct<DK, DV, TI, 32, false>(d, causal);
-        case 64: return obf ? run_fwd_ct<DK, DV, TI, 64, true>(d, causal) : run_fwd_ct<DK, DV, TI, 64, false>(d, causal);
+        case 16: return pick(std::integral_constant<int, 16>{});
+        case 32: return pick(std::integral_constant<int, 32>{});
+        case 64: return pick(std::integral_constant<int, 64>{});
         default: return hipErrorInvalidValue;
     }
 }
