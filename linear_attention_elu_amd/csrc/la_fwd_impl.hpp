@@ -88,6 +88,7 @@ struct FwdParams {
     int seg_base;           // segment of workgroup row blockIdx.y: seg_base + blockIdx.y
     const float *gamma;     // MODE_CAUSAL, MODE_AGG: per-head decay [H], or null for none
     int H;                  // heads (bh % H is the head of workgroup column bh)
+    int sum_P;              // MODE_APPLY: the total state is the sum of slots 0 .. sum_P - 1 (>= 1)
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -439,19 +440,35 @@ la_chunk_kernel(const FwdParams p) {
     }
 
     // S(cb) slices and z in accumulator layout: lane (pp, g) holds rows
-    // 16E + 4g + r; for z every column holds the same value.
+    // 16E + 4g + r; for z every column holds the same value.  The non-causal
+    // read-out sums the per-segment aggregates itself, slot by slot in a fixed
+    // order (a few slots; no separate total pass).
     f32x4 accS[CBW][NE];
     f32x4 accZ[NE];
+    const int nsum = MODE == MODE_APPLY ? p.sum_P : 1;
 #pragma unroll
     for (int E = 0; E < NE; ++E) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accZ[E][r] = zin ? zin[16 * E + 4 * g + r] : 0.0f;
+        for (int r = 0; r < 4; ++r) accZ[E][r] = 0.0f;
 #pragma unroll
-        for (int cs = 0; cs < CBW; ++cs) {
-            const int cb = wave + 4 * cs;
+        for (int cs = 0; cs < CBW; ++cs)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                accS[cs][E][r] = (Sin && col_ok(cs)) ? Sin[(16 * E + 4 * g + r) * DV + 16 * cb + pp] : 0.0f;
+            for (int r = 0; r < 4; ++r) accS[cs][E][r] = 0.0f;
+    }
+    for (int t = 0; t < nsum; ++t) {
+        const float *St = Sin ? Sin + t * (long)(DK * DV + DK) : nullptr;
+        const float *zt = zin ? zin + t * (long)(DK * DV + DK) : nullptr;
+#pragma unroll
+        for (int E = 0; E < NE; ++E) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accZ[E][r] += zt ? zt[16 * E + 4 * g + r] : 0.0f;
+#pragma unroll
+            for (int cs = 0; cs < CBW; ++cs) {
+                const int cb = wave + 4 * cs;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    accS[cs][E][r] += (St && col_ok(cs)) ? St[(16 * E + 4 * g + r) * DV + 16 * cb + pp] : 0.0f;
+            }
         }
     }
 
