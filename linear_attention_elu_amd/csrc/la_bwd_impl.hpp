@@ -47,7 +47,8 @@
 // the same gradient with full sums instead of prefix and suffix sums, so every
 // token reads the totals S, z (dq sweep) and R, r (dk/dv sweep): no masked
 // in-chunk products, no carry, and each sweep loads only the rows it needs
-// (q, dO for dq; k, v for dk, dv).
+// (q, dO for dq; k, v for dk, dv).  The totals come as a few per-segment
+// sums that each workgroup adds up in its prologue, in a fixed order.
 //
 // LDS row strides: tiles read row-wise (two 8-byte pieces per lane, rows p =
 // 0..15) are padded to a stride of 4 (mod 8) times an odd number of banks,
@@ -73,6 +74,7 @@ struct BwdParams {
     int L;                   // tokens per segment of this launch
     int state_P;             // segments per bh in the state array
     int state_mult;          // fine segments per segment of this launch
+    int sum_P;               // non-causal: the totals are the sums of slots 0 .. sum_P - 1
 };
 
 template <typename TI, int DK, int DV> constexpr int bwd_cmax() {
@@ -217,12 +219,15 @@ la_bwd_dq_kernel(const BwdParams p) {
     for (int cv = 0; cv < CV; ++cv) accS[cv] = zero4;
     if (p.state && active) {
         const float *Sin = p.state + (bh * p.state_P + (long)seg * p.state_mult) * (long)(DK * DV + DK);
+        // non-causal: the per-segment sums, added slot by slot in a fixed order
+        for (int t = 0; t < (NC ? p.sum_P : 1); ++t, Sin += DK * DV + DK) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accZ[r] = Sin[DK * DV + 16 * eb + 4 * g + r];
+            for (int r = 0; r < 4; ++r) accZ[r] += Sin[DK * DV + 16 * eb + 4 * g + r];
 #pragma unroll
-        for (int cv = 0; cv < CV; ++cv)
+            for (int cv = 0; cv < CV; ++cv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accS[cv][r] = Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
+                for (int r = 0; r < 4; ++r) accS[cv][r] += Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
+        }
     }
     Frag<TC> fragS[NSV];  // S rows e, split over the value index
     // Non-causal with bf16 operands: the total S also as its rounding
@@ -481,12 +486,14 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         // segment (non-causal: the total, in slot 0)
         const long last = NC ? 0 : min((long)(seg + 1) * p.state_mult, (long)p.state_P) - 1;
         const float *Rin = p.state + (bh * p.state_P + last) * (long)(DK * DV + DK);
+        for (int t = 0; t < (NC ? p.sum_P : 1); ++t, Rin += DK * DV + DK) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accr[r] = Rin[DK * DV + 16 * eb + 4 * g + r];
+            for (int r = 0; r < 4; ++r) accr[r] += Rin[DK * DV + 16 * eb + 4 * g + r];
 #pragma unroll
-        for (int cv = 0; cv < CV; ++cv)
+            for (int cv = 0; cv < CV; ++cv)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accR[cv][r] = Rin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
+                for (int r = 0; r < 4; ++r) accR[cv][r] += Rin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
+        }
     }
     Frag<TC> fragR[NSV];  // R rows e, split over the value index
     // Non-causal with bf16 operands: R also as its rounding remainder, so that

@@ -31,10 +31,10 @@ inline BwdLayout bwd_layout(long BH, int N, int DK, int DV, int Pmax) {
 
 // Gradient of the non-causal form: the totals S, z and R, r replace the
 // prefix and suffix states, so the sequence splits freely.
-//   aggregates of phi(K)^T V, phi(K)^T 1 per segment -> total
-//   dq sweep (non-causal)      leaves 1/den and eps per token
-//   aggregates of (phi(Q)/den)^T dO, (phi(Q)/den)^T e per segment -> total
-//   dk/dv sweep (non-causal)
+//   aggregates of phi(K)^T V, phi(K)^T 1 over a few segments
+//   dq sweep (non-causal; sums them)      leaves 1/den and eps per token
+//   aggregates of (phi(Q)/den)^T dO, (phi(Q)/den)^T e over a few segments
+//   dk/dv sweep (non-causal; sums them)
 template <int DK, int DV, typename TI, int CT>
 hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     const long BH = (long)d.B * d.H;
@@ -53,9 +53,12 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI, true>;
     auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI, true>;
     static OccCache occ_dq, occ_kv;
-    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT>();
     const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), occ_dq, kBwdThreads);
     const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
+    // a few aggregate segments per (b, h), as in the non-causal forward (a
+    // target within kMaxTargetWg keeps Pf within the workspace the query sized)
+    const long target_agg = BH * (long)kNonCausalAggSegments < kMaxTargetWg ? BH * (long)kNonCausalAggSegments
+                                                                             : kMaxTargetWg;
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
 
@@ -69,8 +72,6 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     a.seg_out = tot;
     agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (Pf > 1 && (err = launch_seg_scan(tot, nullptr, nullptr, BH, Pf, DK, DV, 1, Pf, d.stream)) != hipSuccess)
-        return err;
 
     BwdParams b{};
     b.q = d.q;
@@ -85,7 +86,8 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     b.N = d.N;
     b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
     b.state_P = Pf;
-    b.state_mult = 0;  // every segment reads the total in slot 0
+    b.state_mult = 0;  // every segment reads slots 0 .. Pf - 1
+    b.sum_P = Pf;
     int Lq = 0, Lkv = 0;
     const int Pq = plan_segments(BH, d.N, d.C, target_dq, &Lq);
     const int Pkv = plan_segments(BH, d.N, d.C, target_kv, &Lkv);
@@ -102,8 +104,6 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     a.seg_out = rtot;
     aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (Pf > 1 && (err = launch_seg_scan(rtot, nullptr, nullptr, BH, Pf, DK, DV, 1, Pf, d.stream)) != hipSuccess)
-        return err;
 
     b.state = rtot;
     b.L = Lkv;
