@@ -390,6 +390,10 @@ def main():
                  "flops_per_launch": f["flops"]},
     }
     log(f"fwd {f['ms'] * 1e3:.1f} us/step, {f['gbs']:.0f} GB/s")
+    # what a plain device copy reaches on this part, next to the spec peak (context only)
+    cp = bench_copy(dev, 1024, steps=10, warmup=3)
+    res["hbm_context"] = {"device_copy_GBs": cp["GBs"], "spec_peak_GBs": HBM_PEAK_GBS,
+                          "copy": "1 GiB read + 1 GiB written per copy, torch copy_ on the device"}
     if not args.no_decode:
         log("decode: 3072 steps, graph replay")
         res["decode"] = bench_decode(dev)
