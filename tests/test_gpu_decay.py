@@ -137,3 +137,30 @@ def test_decay_workload_sampled():
         err = row_rel_l2(to64(o[sl]), ref)
         print(f"(b={b}, h={h}) row-wise relative L2 {err:.3e}")
         assert err <= 2e-2, (b, h, err)
+
+
+@pytest.mark.parametrize("decay", [False, True])
+def test_handoff_with_one_segment_per_sequence(decay):
+    """With B*H large enough to fill the GPU on its own, each (batch, head) runs
+    as one segment and the carried state enters the chunk loop directly (no
+    scan): two calls over the halves of a sequence still match the oracle."""
+    dev = need_gpu()
+    B, H, N, dk, dv = 16, 16, 300, 32, 32
+    announce(f"one-segment handoff decay={decay}")
+    x, x64 = device_inputs(B, H, N, dk, dv, "f32", seed=17)
+    g = torch.tensor(np.linspace(0.6, 1.0, H), dtype=torch.float32, device=dev)
+    h = 130
+    S = torch.empty(B, H, dk, dv, device=dev)
+    z = torch.empty(B, H, dk, device=dev)
+    first = [t[:, :, :h].contiguous() for t in (x["q"], x["k"], x["v"])]
+    second = [t[:, :, h:].contiguous() for t in (x["q"], x["k"], x["v"])]
+    if decay:
+        o1, _ = la.la_fwd_causal_decay(*first, g, S_out=S, z_out=z, C=32)
+        o2, _ = la.la_fwd_causal_decay(*second, g, S0=S, z0=z, S_out=S, z_out=z, C=32)
+        ref, _ = oracle.fwd_causal_decay(x64["q"], x64["k"], x64["v"], g.cpu().double().numpy())
+    else:
+        o1, _ = la.la_fwd_causal_state(*first, S_out=S, z_out=z, C=32)
+        o2, _ = la.la_fwd_causal_state(*second, S0=S, z0=z, S_out=S, z_out=z, C=32)
+        ref, _ = oracle.fwd_causal(x64["q"], x64["k"], x64["v"])
+    torch.cuda.synchronize(dev)
+    assert_close(np.concatenate([to64(o1), to64(o2)], axis=2), ref, "f32", "out")
