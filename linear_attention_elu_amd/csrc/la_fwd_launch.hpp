@@ -24,16 +24,17 @@ long chunk_resident() {
 // apiece), against 26.9 us with a separate total pass.
 constexpr int kNonCausalAggSegments = 4;
 
-// DECAY: the causal form with a per-head decay (d.gamma non-null).
-template <int DK, int DV, typename TI, int CT, bool OBF, bool DECAY>
+// DECAY: the causal form with a per-head decay (d.gamma non-null).  CT: the
+// chunk of the causal and read-out kernels; CTA: that of the aggregate pass.
+template <int DK, int DV, typename TI, int CT, int CTA, bool OBF, bool DECAY>
 hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CT, false, DECAY>;
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CTA, false, DECAY>;
     auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>
                               : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
-    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CT, false, DECAY>();
+    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY>();
     const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>()
                                     : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF>();
     int Lf = 0;
@@ -105,29 +106,41 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     return hipGetLastError();
 }
 
-// Chunk size the kernels run at for a requested C: fp32 operands with a
-// 128-wide head dimension tile 64-token chunks as two of 32 (registers); the
-// result does not depend on the chunk size, and segment lengths stay
-// multiples of the requested C.
+// Chunk sizes the kernels run at for a requested C.  The result does not
+// depend on them, and segment lengths stay multiples of the requested C.
+//   fwd_chunk: the aggregate passes (forward and backward); fp32 operands
+//     with a 128-wide head dimension tile 64-token chunks as two of 32.
+//   fwd_main_chunk: the causal chunk loop and the read-out; every 128-wide
+//     head dimension tiles at 32 (the four-wave bf16 causal kernel spills at
+//     64 and runs 5% faster at 32; its aggregate pass runs faster at 64).
 template <int DK, int DV, typename TI> constexpr int fwd_chunk(int C) {
     return (sizeof(TI) == 4 && (DK == 128 || DV == 128) && C > 32) ? 32 : C;
+}
+template <int DK, int DV, typename TI> constexpr int fwd_main_chunk(int C) {
+    return ((DK == 128 || DV == 128) && C > 32) ? 32 : C;
 }
 
 template <int DK, int DV, typename TI>
 hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     const bool obf = d.out_bf16 != 0;
     const bool dec = causal && d.gamma != nullptr;
-    auto pick = [&](auto ct) {
-        constexpr int CT = decltype(ct)::value;
-        if (dec) return obf ? run_fwd_ct<DK, DV, TI, CT, true, true>(d, causal)
-                            : run_fwd_ct<DK, DV, TI, CT, false, true>(d, causal);
-        return obf ? run_fwd_ct<DK, DV, TI, CT, true, false>(d, causal)
-                   : run_fwd_ct<DK, DV, TI, CT, false, false>(d, causal);
+    auto pick = [&](auto ct, auto cta) {
+        constexpr int CT = decltype(ct)::value, CTA = decltype(cta)::value;
+        if (dec) return obf ? run_fwd_ct<DK, DV, TI, CT, CTA, true, true>(d, causal)
+                            : run_fwd_ct<DK, DV, TI, CT, CTA, false, true>(d, causal);
+        return obf ? run_fwd_ct<DK, DV, TI, CT, CTA, true, false>(d, causal)
+                   : run_fwd_ct<DK, DV, TI, CT, CTA, false, false>(d, causal);
     };
-    switch (fwd_chunk<DK, DV, TI>(d.C)) {
-        case 16: return pick(std::integral_constant<int, 16>{});
-        case 32: return pick(std::integral_constant<int, 32>{});
-        case 64: return pick(std::integral_constant<int, 64>{});
+    using I16 = std::integral_constant<int, 16>;
+    using I32 = std::integral_constant<int, 32>;
+    using I64 = std::integral_constant<int, 64>;
+    if constexpr (sizeof(TI) == 2 && (DK == 128 || DV == 128)) {
+        if (fwd_main_chunk<DK, DV, TI>(d.C) == 32 && fwd_chunk<DK, DV, TI>(d.C) == 64) return pick(I32{}, I64{});
+    }
+    switch (fwd_main_chunk<DK, DV, TI>(d.C)) {
+        case 16: return pick(I16{}, I16{});
+        case 32: return pick(I32{}, I32{});
+        case 64: return pick(I64{}, I64{});
         default: return hipErrorInvalidValue;
     }
 }
