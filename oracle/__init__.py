@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     bwd_noncausal,
     fwd_causal_decay,
     decode_step_decay,
+    bwd_causal_decay,
     num_threads,
     library_path,
     load_variant,

@@ -445,3 +445,82 @@ void oracle_decode_step_decay_f64(double *S, double *z, const double *q, const d
         }
     }
 }
+
+/*
+ * Gradient of the causal form with the per-head decay (the itwiki variants
+ * table, RetNet row; the pages print no gradient).  It is the cumulative-sum
+ * gradient above with both running sums decayed by gamma_h per token:
+ *   S'_i = gamma S'_{i-1} + phi(k_i) V'_i^T      dL/dphi(q_i) = S'_i G'_i
+ *   R'_j = gamma R'_{j+1} + phi(q_j) G'_j^T      dL/dphi(k_j) = R'_j V'_j,
+ *                                                dL/dv_j = R_j^T phi(k_j),
+ * with V'_j = [v_j, 1], G'_i = [g_i / den_i, -(g_i . out_i) / den_i] and the
+ * decayed den_i, out_i of oracle_fwd_causal_decay_f64; then the chain rule
+ * through phi.  gamma = 1 is oracle_bwd_causal_f64.
+ */
+void oracle_bwd_causal_decay_f64(const double *q, const double *k, const double *v, const double *g,
+                                 const double *gamma, double *dq, double *dk_out, double *dv_out,
+                                 int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int dv1 = dv + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double gm = gamma[bh % H];
+        const double *qb = q + bh * (long)N * dk;
+        const double *kb = k + bh * (long)N * dk;
+        const double *vb = v + bh * (long)N * dv;
+        const double *gb = g + bh * (long)N * dv;
+        double *dqb = dq + bh * (long)N * dk;
+        double *dkb = dk_out + bh * (long)N * dk;
+        double *dvb = dv_out + bh * (long)N * dv;
+        double *Gp = malloc((size_t)N * dv1 * sizeof(double));
+        double *Sp = calloc((size_t)dk * dv1, sizeof(double));
+
+        /* Forward sweep: decayed S', out_i and den_i, G'_i, then dq_i = (S'_i G'_i) phi'(q_i). */
+        for (int i = 0; i < N; ++i) {
+            for (int e = 0; e < dk; ++e) {
+                double fk = phi(kb[(long)i * dk + e]);
+                for (int c = 0; c < dv; ++c)
+                    Sp[(long)e * dv1 + c] = gm * Sp[(long)e * dv1 + c] + fk * vb[(long)i * dv + c];
+                Sp[(long)e * dv1 + dv] = gm * Sp[(long)e * dv1 + dv] + fk;
+            }
+            double d = 0.0;
+            for (int e = 0; e < dk; ++e) d += phi(qb[(long)i * dk + e]) * Sp[(long)e * dv1 + dv];
+            double go = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < dk; ++e) num += phi(qb[(long)i * dk + e]) * Sp[(long)e * dv1 + c];
+                go += gb[(long)i * dv + c] * (num / d);
+                Gp[(long)i * dv1 + c] = gb[(long)i * dv + c] / d;
+            }
+            Gp[(long)i * dv1 + dv] = -go / d;
+            for (int e = 0; e < dk; ++e) {
+                double acc = 0.0;
+                for (int c = 0; c < dv1; ++c) acc += Sp[(long)e * dv1 + c] * Gp[(long)i * dv1 + c];
+                dqb[(long)i * dk + e] = acc * dphi(qb[(long)i * dk + e]);
+            }
+        }
+
+        /* Reverse sweep: decayed R', then dk_j and dv_j. */
+        memset(Sp, 0, (size_t)dk * dv1 * sizeof(double));
+        for (int j = N - 1; j >= 0; --j) {
+            for (int e = 0; e < dk; ++e) {
+                double fq = phi(qb[(long)j * dk + e]);
+                for (int c = 0; c < dv1; ++c)
+                    Sp[(long)e * dv1 + c] = gm * Sp[(long)e * dv1 + c] + fq * Gp[(long)j * dv1 + c];
+            }
+            for (int e = 0; e < dk; ++e) {
+                double acc = Sp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */
+                for (int c = 0; c < dv; ++c) acc += Sp[(long)e * dv1 + c] * vb[(long)j * dv + c];
+                dkb[(long)j * dk + e] = acc * dphi(kb[(long)j * dk + e]);
+            }
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int e = 0; e < dk; ++e) acc += Sp[(long)e * dv1 + c] * phi(kb[(long)j * dk + e]);
+                dvb[(long)j * dv + c] = acc;
+            }
+        }
+        free(Gp);
+        free(Sp);
+    }
+}

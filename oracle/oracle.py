@@ -45,6 +45,7 @@ def _bind(path: str):
     lib.oracle_bwd_noncausal_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_fwd_causal_decay_f64.argtypes = [P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_decode_step_decay_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i]
+    lib.oracle_bwd_causal_decay_f64.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -167,6 +168,21 @@ def decode_step_decay(S, z, q, k, v, gamma, lib=None):
     (lib or _load()).oracle_decode_step_decay_f64(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o),
                                          B, H, dk, dv)
     return S, z, o
+
+
+def bwd_causal_decay(q, k, v, dout, gamma, lib=None):
+    """Exact gradient of the causal forward with a fixed decay gamma[h] per head: (dq, dk, dv)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    gm = _f64(np.asarray(gamma, dtype=np.float64).reshape(-1))
+    assert g.shape == v.shape and gm.shape == (H,)
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    (lib or _load()).oracle_bwd_causal_decay_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gm), _ptr(dq), _ptr(dkk),
+                                        _ptr(dvv), B, H, N, dk, dv)
+    return dq, dkk, dvv
 
 
 def load_variant(path: str):

@@ -241,8 +241,40 @@ def check_decay(lib=None):
     np.testing.assert_allclose(z, (fk * w[..., None]).sum(2), rtol=1e-12)
 
 
+def check_backward_decay(lib=None):
+    """Decayed gradient == central finite differences of the decay-masked
+    quadratic form; gamma = 1 gives the causal gradient; gamma = 0 makes
+    out = v, so dq = dk = 0 and dv = dO; value gradients sum to the upstream ones."""
+    B, H, N, dk, dv = 1, 2, 9, 3, 4
+    q, k, v = _qkv(B, H, N, dk, dv, seed=41)
+    g = _rng(42).standard_normal(v.shape)
+    gam = np.array([0.6, 0.95])
+    dq, dkk, dvv = oracle.bwd_causal_decay(q, k, v, g, gam, lib=lib)
+
+    def loss_q(x):
+        return float((forms.causal_quadratic_decay(x, k, v, gam)[0] * g).sum())
+
+    def loss_k(x):
+        return float((forms.causal_quadratic_decay(q, x, v, gam)[0] * g).sum())
+
+    def loss_v(x):
+        return float((forms.causal_quadratic_decay(q, k, x, gam)[0] * g).sum())
+
+    for got, f, x in ((dq, loss_q, q), (dkk, loss_k, k), (dvv, loss_v, v)):
+        ref = forms.fd_gradient(f, x.copy())
+        err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+        assert err < 1e-6, f"finite-difference mismatch {err:.3e}"
+    np.testing.assert_allclose(dvv.sum(2), g.sum(2), rtol=1e-12, atol=1e-12)
+    for a, b in zip(oracle.bwd_causal_decay(q, k, v, g, np.ones(2), lib=lib), oracle.bwd_causal(q, k, v, g, lib=lib)):
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+    z0 = oracle.bwd_causal_decay(q, k, v, g, np.zeros(2), lib=lib)
+    assert np.abs(z0[0]).max() < 1e-13 and np.abs(z0[1]).max() < 1e-13
+    np.testing.assert_allclose(z0[2], g, rtol=1e-13, atol=1e-14)
+
+
 ALL_CHECKS = [check_golden, check_causal_vs_quadratic, check_causal_vs_chunked, check_noncausal,
-              check_invariants, check_decode, check_backward, check_backward_noncausal, check_decay]
+              check_invariants, check_decode, check_backward, check_backward_noncausal, check_decay,
+              check_backward_decay]
 
 
 def failing_checks(lib):

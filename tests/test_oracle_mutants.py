@@ -67,6 +67,10 @@ MUTANTS = {
                              "const double g = gamma[(bh / H) % H];\n        const double *qb = q + bh * (long)N * dk;"),
     "decode_decay_misses_S": ("Sb[(long)e * dv + c] = g * Sb[(long)e * dv + c] + fk * vb[c];",
                               "Sb[(long)e * dv + c] = Sb[(long)e * dv + c] + fk * vb[c];"),
+    "dbwd_reverse_undecayed": ("Sp[(long)e * dv1 + c] = gm * Sp[(long)e * dv1 + c] + fq * Gp[(long)j * dv1 + c];",
+                               "Sp[(long)e * dv1 + c] = Sp[(long)e * dv1 + c] + fq * Gp[(long)j * dv1 + c];"),
+    "dbwd_z_undecayed": ("Sp[(long)e * dv1 + dv] = gm * Sp[(long)e * dv1 + dv] + fk;",
+                         "Sp[(long)e * dv1 + dv] = Sp[(long)e * dv1 + dv] + fk;"),
     "nbwd_eps_sign": ("Gi[dv] = -go / d;", "Gi[dv] = go / d;"),
     "nbwd_drops_ones_column": ("double acc = Rp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */",
                                "double acc = 0.0;"),
