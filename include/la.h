@@ -21,14 +21,16 @@
  *     "key components 4)"; velog 3.6; itwiki "Causal masking and the
  *     recurrent form";
  *   - gradient as cumulative sums with linear memory: velog 3.5; blog digest
- *     "Methods" (last item).
+ *     "Methods" (last item);
+ *   - fixed per-head decay of the state: itwiki, table of later variants,
+ *     RetNet row (la_fwd_causal_decay, la_decode_step_decay).
  *
  * Conventions shared by every entry point
  *   Layout    All tensors are dense, row-major and contiguous:
  *             sequences [B][H][N][d], state S [B][H][d_k][d_v],
  *             normaliser z [B][H][d_k], per-token denominators [B][H][N],
- *             per-step decode vectors [B][H][d].  Every pointer must be
- *             16-byte aligned.
+ *             per-step decode vectors [B][H][d], per-head decays [H].
+ *             Every tensor pointer must be 16-byte aligned (gamma: 4-byte).
  *   Sizes     d_k, d_v in {16, 32, 64, 128}, chosen independently; N >= 1 and
  *             need not be a multiple of C; C in {16, 32, 64}; B, H >= 1.
  *   Dtypes    `in` is the storage type of q, k, v (and dO, dq, dk, dv);
