@@ -44,11 +44,23 @@
  *             and returns; results are ready when the stream has reached it.
  *   Errors    All arguments are checked before anything is enqueued; a bad
  *             argument returns a non-zero la_status and launches nothing.  A
- *             failed launch returns LA_ERR_LAUNCH.  NaN or Inf inputs are
- *             propagated, not reported.  No C++ exception crosses the ABI.
- *             No denominator epsilon is added: inputs below about -87 make
- *             exp underflow in fp32, and a zero denominator then yields Inf
- *             or NaN, as the formulas imply.
+ *             failed launch returns LA_ERR_LAUNCH.  No C++ exception crosses
+ *             the ABI.
+ *   Non-finite values are propagated, not reported.  In the causal forward a
+ *             NaN or +Inf in q at token i makes out_i (and den_i) non-finite
+ *             and nothing else; in k or v at token j it makes every output at
+ *             and after j of that (b, h) non-finite, leaves every output
+ *             before the C-token chunk holding j unchanged, and may reach the
+ *             earlier tokens of that chunk (a masked product with a zero
+ *             weight still carries a NaN).  -Inf in k is phi = 0: a token
+ *             without weight.  The non-causal form spreads a non-finite k or v
+ *             to every output of its (b, h); the decode step spreads a
+ *             non-finite k or v into S and z, and so into every later step.
+ *             Other (b, h) pairs are never affected.
+ *   Underflow No denominator epsilon is added: phi(x) = exp(x) underflows to 0
+ *             in fp32 below about -87 (-104 with subnormals), so a query whose
+ *             entries all lie below that has den = 0 and a non-finite output,
+ *             as the formulas imply.
  */
 #ifndef LA_H
 #define LA_H

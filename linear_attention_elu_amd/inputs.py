@@ -20,14 +20,21 @@ def normals(shapes: Sequence[Tuple[int, ...]], seed: int = 0) -> Tuple[np.ndarra
 
 
 def attention_inputs(B: int, H: int, N: int, dk: int, dv: int, seed: int = 0,
-                     with_grad: bool = False) -> Dict[str, np.ndarray]:
-    """q, k [B,H,N,dk], v [B,H,N,dv] (and dO [B,H,N,dv]) as float32."""
+                     with_grad: bool = False, qk_std: float = 1.0) -> Dict[str, np.ndarray]:
+    """q, k [B,H,N,dk], v [B,H,N,dv] (and dO [B,H,N,dv]) as float32.
+
+    q and k are drawn from N(0, qk_std^2) (the unit draws times qk_std, in
+    float32); v and dO are unit normals."""
     shapes = [(B, H, N, dk), (B, H, N, dk), (B, H, N, dv)]
     names = ["q", "k", "v"]
     if with_grad:
         shapes.append((B, H, N, dv))
         names.append("dO")
-    return dict(zip(names, normals(shapes, seed)))
+    out = dict(zip(names, normals(shapes, seed)))
+    if qk_std != 1.0:
+        for n in ("q", "k"):
+            out[n] *= np.float32(qk_std)
+    return out
 
 
 def decode_inputs(T: int, B: int, H: int, dk: int, dv: int, seed: int = 0) -> Dict[str, np.ndarray]:

@@ -3,14 +3,23 @@ copies of what the device saw, and the error measures the tolerances use.
 
 Tolerances (the same for every parity test):
 - fp32 inputs: elementwise max |gpu - oracle| <= 1e-4;
-- bf16 inputs: row-wise relative L2, max over rows of
-  ||gpu_i - oracle_i||_2 / max(||oracle_i||_2, m) <= 2e-2, where m is the
-  median row norm of the compared block.  The floor only matters for rows
-  whose exact value cancels to (near) zero -- e.g. dq of the first token is
-  exactly zero because out_0 = v_0 -- where a purely relative measure is
-  undefined; there the error is measured against the typical row.  When every
-  row cancels (a single token: all gradients are exactly zero), an absolute
-  floor given by the caller takes over.
+- bf16 inputs: row-wise relative L2, max over rows i of
+  ||gpu_i - oracle_i||_2 / ||oracle_i||_2 <= 2e-2, strictly, for every row
+  whose exact value is not zero.
+
+Rows whose exact value is zero.  The first token's dq is exactly 0 for any
+q_0, k_0 (out_0 = v_0), and so is every gradient of a one-token sequence; the
+terms that cancel in them are of ordinary size, so rounding leaves a small
+residue and a relative error is undefined.  These rows, recognised by an
+fp64 norm below ZERO_ROW * (median row norm), are held to an absolute bound
+instead: ||gpu_i - oracle_i||_2 <= 2e-2 * max(ZERO_SCALE * (median row norm),
+abs_floor), abs_floor being the caller's scale for blocks whose every row is
+zero (the median is then itself a rounding residue).  No other row is
+relaxed.  (Measured with the oracle: apart from those rows, the larger of the
+two terms that cancel in a dq or dk row is at most 4.2x the row's norm, and the
+smallest rows that do not cancel -- the last tokens' dk and dv, whose suffix
+sums hold few terms -- sit at 1.6e-4 of the median at N = 65536, far above
+ZERO_ROW.)  Every check prints the strict maximum and how many zero rows it met.
 """
 from __future__ import annotations
 
@@ -24,6 +33,8 @@ from linear_attention_elu_amd import inputs
 
 FP32_MAX_ABS = 1e-4
 BF16_ROW_REL = 2e-2
+ZERO_ROW = 1e-9
+ZERO_SCALE = 1e-2
 
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -38,9 +49,16 @@ def announce(msg: str) -> None:
     print(f"[case] {msg}", file=sys.stderr, flush=True)
 
 
-def device_inputs(B, H, N, dk, dv, dtype, seed=0, with_grad=False, device="cuda:0", exact=True):
-    """Seeded inputs on the device plus (if `exact`) their exact float64 host copies."""
-    host = inputs.attention_inputs(B, H, N, dk, dv, seed=seed, with_grad=with_grad)
+def report(msg: str) -> None:
+    print(f"[err] {msg}", file=sys.stderr, flush=True)
+
+
+def device_inputs(B, H, N, dk, dv, dtype, seed=0, with_grad=False, device="cuda:0", exact=True, scale=1.0):
+    """Seeded inputs on the device plus (if `exact`) their exact float64 host copies.
+
+    `scale` is the standard deviation of q and k (wide-range inputs); v and dO
+    stay unit normals."""
+    host = inputs.attention_inputs(B, H, N, dk, dv, seed=seed, with_grad=with_grad, qk_std=scale)
     dev = {n: inputs.to_torch(a, DTYPES[dtype], device) for n, a in host.items()}
     del host
     if not exact:
@@ -56,21 +74,43 @@ def max_abs(a, b) -> float:
     return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max()) if np.size(a) else 0.0
 
 
-def row_rel_l2(a, b, abs_floor: float = 1e-300) -> float:
+def row_errors(a, b, abs_floor: float = 0.0):
+    """(measure, strict max over nonzero rows, zero rows, rows) of the bf16 check.
+
+    The measure is the maximum over nonzero rows of the relative L2 error and
+    over zero rows of the absolute L2 error divided by the zero-row scale."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
-    num = np.sqrt(((a - b) ** 2).sum(-1))
-    den = np.sqrt((b ** 2).sum(-1))
+    num = np.sqrt(((a - b) ** 2).sum(-1)).reshape(-1)
+    den = np.sqrt((b ** 2).sum(-1)).reshape(-1)
     if not num.size:
-        return 0.0
-    floor = max(float(np.median(den)), abs_floor)
-    return float((num / np.maximum(den, floor)).max())
+        return 0.0, 0.0, 0, 0
+    med = float(np.median(den))
+    zero = den <= ZERO_ROW * max(med, abs_floor)
+    strict = float((num[~zero] / den[~zero]).max()) if (~zero).any() else 0.0
+    measure = strict
+    if zero.any():
+        scale = max(ZERO_SCALE * med, abs_floor)
+        assert scale > 0, "a block whose rows are all zero needs an absolute floor"
+        measure = max(measure, float(num[zero].max()) / scale)
+    return measure, strict, int(zero.sum()), int(num.size)
 
 
-def assert_close(got, ref, dtype: str, what: str = "", abs_floor: float = 1e-300) -> None:
+def row_rel_l2(a, b, abs_floor: float = 0.0) -> float:
+    return row_errors(a, b, abs_floor)[0]
+
+
+def check_rows(got, ref, what: str = "", abs_floor: float = 0.0, tol: float = BF16_ROW_REL) -> float:
+    err, strict, nz, n = row_errors(got, ref, abs_floor)
+    report(f"{what}: row-wise relative L2 {strict:.3e} strict over {n - nz} rows; {nz} zero rows; measure {err:.3e}")
+    assert err <= tol, f"{what}: measure {err:.3e} > {tol} (strict {strict:.3e}, {nz} zero rows)"
+    return err
+
+
+def assert_close(got, ref, dtype: str, what: str = "", abs_floor: float = 0.0) -> None:
     if dtype == "f32":
         err = max_abs(got, ref)
+        report(f"{what}: max abs error {err:.3e}")
         assert err <= FP32_MAX_ABS, f"{what}: max abs error {err:.3e} > {FP32_MAX_ABS}"
     else:
-        err = row_rel_l2(got, ref, abs_floor)
-        assert err <= BF16_ROW_REL, f"{what}: row-wise relative L2 {err:.3e} > {BF16_ROW_REL}"
+        check_rows(got, ref, what, abs_floor)

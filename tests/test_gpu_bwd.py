@@ -5,7 +5,7 @@ import torch
 
 import linear_attention_elu_amd as la
 import oracle
-from gpu_util import announce, assert_close, device_inputs, max_abs, need_gpu, row_rel_l2, to64
+from gpu_util import announce, assert_close, check_rows, device_inputs, max_abs, need_gpu, report, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -43,23 +43,48 @@ def test_backward_matches_oracle(case, dtype):
     assert_close(to64(dvv), rv, dtype, "dv", abs_floor=1e-3)
 
 
-def test_backward_workload_sampled():
-    """Causal forward + backward at B=8, H=16, N=8192, d=128, C=64, bf16, seed 0,
-    as the benchmark runs it; the oracle checks every row of three sampled
-    (batch, head) pairs."""
+def test_backward_workload_every_head():
+    """Causal backward at B=8, H=16, N=8192, d=128, C=64, bf16, seed 0, as the
+    benchmark runs it: every row of dq, dk and dv of every (batch, head) against
+    the oracle."""
     dev = need_gpu()
     B, H, N, d = 8, 16, 8192, 128
     announce("bwd workload")
     x, _ = device_inputs(B, H, N, d, d, "bf16", seed=0, with_grad=True, exact=False)
     dq, dkk, dvv = run_bwd(x, 64)
     torch.cuda.synchronize(dev)
-    for (b, h) in [(0, 0), (4, 9), (7, 15)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
+    for b in range(B):
+        sl = slice(b, b + 1)
         rq, rk, rv = oracle.bwd_causal(*(to64(x[n][sl]) for n in ("q", "k", "v", "dO")))
         for name, got, ref in (("dq", dq, rq), ("dk", dkk, rk), ("dv", dvv, rv)):
-            err = row_rel_l2(to64(got[sl]), ref)
-            print(f"(b={b}, h={h}) {name}: row-wise relative L2 {err:.3e}")
-            assert err <= 2e-2, (b, h, name, err)
+            check_rows(to64(got[sl]), ref, f"batch {b} {name}")
+
+
+WIDE_BWD_CASES = [(1, 2, 1000, 64, 64, 64), (1, 2, 5000, 64, 32, 64), (1, 1, 700, 128, 128, 64)]
+
+
+@pytest.mark.parametrize("std", [4.0, 8.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", WIDE_BWD_CASES, ids=lambda c: "B{}_H{}_N{}_dk{}_dv{}_C{}".format(*c))
+def test_backward_wide_range_inputs(case, dtype, std):
+    """q, k ~ N(0, std^2): phi and phi' span e^-30 .. 30."""
+    dev = need_gpu()
+    B, H, N, dk, dv, C = case
+    announce(f"wide-range bwd {dtype} std={std} {case}")
+    x, x64 = device_inputs(B, H, N, dk, dv, dtype, seed=sum(case) + int(std), with_grad=True, scale=std)
+    dq, dkk, dvv = run_bwd(x, C)
+    torch.cuda.synchronize(dev)
+    rq, rk, rv = oracle.bwd_causal(x64["q"], x64["k"], x64["v"], x64["dO"])
+    if dtype == "f32":
+        # gradients grow with the weights' range: hold fp32 to 1e-4 of each block's largest entry
+        for name, got, ref in (("dq", dq, rq), ("dk", dkk, rk), ("dv", dvv, rv)):
+            err = max_abs(to64(got), ref) / max(1.0, float(np.abs(ref).max()))
+            report(f"{name}: max abs error / max(1, max |ref|) {err:.3e}")
+            assert err <= 1e-4, (name, err)
+    else:
+        assert_close(to64(dq), rq, dtype, "dq")
+        assert_close(to64(dkk), rk, dtype, "dk")
+        assert_close(to64(dvv), rv, dtype, "dv")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -6,7 +6,7 @@ import torch
 
 import linear_attention_elu_amd as la
 import oracle
-from gpu_util import announce, assert_close, device_inputs, need_gpu, row_rel_l2, to64
+from gpu_util import announce, assert_close, check_rows, device_inputs, need_gpu, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -119,10 +119,10 @@ def test_decay_prefill_then_decode(dtype):
     assert_close(to64(torch.stack(outs, 2)), ref[:, :, N:], dtype, "decode")
 
 
-def test_decay_workload_sampled():
+def test_decay_workload_every_head():
     """The headline shape B=8, H=8, N=65536, d=64, C=64, bf16, seed 0, with
-    decays 1 - 2^-(3 + h); every row of three sampled (batch, head) pairs
-    against the oracle."""
+    decays 1 - 2^-(3 + h), as the benchmark runs it: every row of every
+    (batch, head) against the oracle."""
     dev = need_gpu()
     B, H, N, d = 8, 8, 65536, 64
     announce("decay workload")
@@ -131,12 +131,10 @@ def test_decay_workload_sampled():
     o, _ = la.la_fwd_causal_decay(x["q"], x["k"], x["v"], g, C=64, want_den=False)
     torch.cuda.synchronize(dev)
     g64 = g.cpu().double().numpy()
-    for (b, h) in [(0, 0), (3, 5), (7, 7)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref, _ = oracle.fwd_causal_decay(*(to64(x[n][sl]) for n in ("q", "k", "v")), g64[h:h + 1])
-        err = row_rel_l2(to64(o[sl]), ref)
-        print(f"(b={b}, h={h}) row-wise relative L2 {err:.3e}")
-        assert err <= 2e-2, (b, h, err)
+    for b0 in range(0, B, 2):
+        sl = slice(b0, b0 + 2)
+        ref, _ = oracle.fwd_causal_decay(*(to64(x[n][sl]) for n in ("q", "k", "v")), g64)
+        check_rows(to64(o[sl]), ref, f"batches {b0}..{b0 + 1}")
 
 
 @pytest.mark.parametrize("decay", [False, True])

@@ -5,7 +5,7 @@ import torch
 
 import linear_attention_elu_amd as la
 import oracle
-from gpu_util import announce, assert_close, device_inputs, max_abs, need_gpu, row_rel_l2, to64
+from gpu_util import announce, assert_close, device_inputs, max_abs, need_gpu, report, to64
 from linear_attention_elu_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -35,9 +35,11 @@ def test_decode_steps_match_oracle(dims, dtype):
     np.testing.assert_allclose(to64(z), zo, rtol=1e-5)
 
 
-def test_decode_workload_sampled():
+def test_decode_workload_every_state():
     """3072 steps at B=256, H=8, d=32, fp32, seed 0 (the 32x32x3 pixel-generation
-    shape); the oracle follows 24 sampled (batch, head) states through every step."""
+    shape): every output of every step of all 2048 (batch, head) states, and every
+    final state, against the oracle (whose causal forward equals T decode steps
+    from zero)."""
     dev = need_gpu()
     T, B, H, d = 3072, 256, 8, 32
     announce("decode workload 3072 steps")
@@ -49,22 +51,61 @@ def test_decode_workload_sampled():
     for t in range(T):
         la.la_decode_step(S, z, q[t], k[t], v[t], o=outs[t])
     torch.cuda.synchronize(dev)
-    rng = np.random.default_rng(1)
-    bs = rng.integers(0, B, 24)
-    hs = rng.integers(0, H, 24)
-    # the oracle's causal forward equals T decode steps from zero
-    qs = np.stack([host["q"][:, b, h] for b, h in zip(bs, hs)])[:, None].astype(np.float64)
-    ks = np.stack([host["k"][:, b, h] for b, h in zip(bs, hs)])[:, None].astype(np.float64)
-    vs = np.stack([host["v"][:, b, h] for b, h in zip(bs, hs)])[:, None].astype(np.float64)
-    ref, _ = oracle.fwd_causal(qs, ks, vs)
-    got = np.stack([to64(outs[:, b, h]) for b, h in zip(bs, hs)])[:, None]
-    err = max_abs(got, ref)
-    print(f"max abs error over 3072 steps: {err:.3e}")
-    assert err <= 1e-4
-    S_ref = np.einsum("ste,stc->sec", np.where(ks[:, 0] > 0, ks[:, 0] + 1, np.exp(np.minimum(ks[:, 0], 0))),
-                      vs[:, 0])
-    S_got = np.stack([to64(S[b, h]) for b, h in zip(bs, hs)])
-    assert np.abs(S_got - S_ref).max() / np.abs(S_ref).max() < 1e-5
+    got = to64(outs)
+    S_got, z_got = to64(S), to64(z)
+    worst = 0.0
+    for b0 in range(0, B, 32):  # [T, B, H, d] -> [B, H, T, d], 32 batches at a time
+        seq = [np.ascontiguousarray(host[n][:, b0:b0 + 32].transpose(1, 2, 0, 3)).astype(np.float64)
+               for n in ("q", "k", "v")]
+        ref, _ = oracle.fwd_causal(*seq)
+        worst = max(worst, max_abs(got[:, b0:b0 + 32].transpose(1, 2, 0, 3), ref))
+        fk = np.where(seq[1] > 0, seq[1] + 1, np.exp(np.minimum(seq[1], 0)))
+        S_sum = np.einsum("bhte,bhtc->bhec", fk, seq[2])
+        assert np.abs(S_got[b0:b0 + 32] - S_sum).max() / np.abs(S_sum).max() < 1e-5
+        np.testing.assert_allclose(z_got[b0:b0 + 32], fk.sum(2), rtol=1e-5)
+    report(f"decode: max abs error over 3072 steps and 2048 states {worst:.3e}")
+    assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("std", [4.0, 8.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_wide_range_inputs(dtype, std):
+    dev = need_gpu()
+    B, H, T, dk, dv = 2, 3, 64, 64, 32
+    announce(f"wide-range decode {dtype} std={std}")
+    x, x64 = device_inputs(B, H, T, dk, dv, dtype, seed=int(std), scale=std)
+    S = torch.zeros(B, H, dk, dv, device=dev)
+    z = torch.zeros(B, H, dk, device=dev)
+    outs = [la.la_decode_step(S, z, *(x[n][:, :, t].contiguous() for n in ("q", "k", "v"))) for t in range(T)]
+    torch.cuda.synchronize(dev)
+    ref, _ = oracle.fwd_causal(x64["q"], x64["k"], x64["v"])
+    assert_close(np.stack([to64(o) for o in outs], 2), ref, dtype, "decode")
+
+
+def test_decode_nonfinite_inputs_propagate():
+    """NaN in q at a step makes that step's output alone non-finite; NaN in k or v
+    makes the state, and so every later output of that (batch, head), non-finite.
+    Other (batch, head) pairs keep their values."""
+    dev = need_gpu()
+    B, H, T, d = 1, 3, 12, 32
+    x, x64 = device_inputs(B, H, T, d, d, "f32", seed=14)
+    for h, name in enumerate(("q", "k", "v")):
+        x[name][0, h, 5, 3] = float("nan")
+    S = torch.zeros(B, H, d, d, device=dev)
+    z = torch.zeros(B, H, d, device=dev)
+    outs = np.stack([to64(la.la_decode_step(S, z, *(x[n][:, :, t].contiguous() for n in ("q", "k", "v"))))
+                     for t in range(T)], 2)[0]
+    torch.cuda.synchronize(dev)
+    ref, _ = oracle.fwd_causal(x64["q"], x64["k"], x64["v"])
+    ref = ref[0]
+    assert not np.isfinite(outs[0, 5]).any()
+    keep = np.arange(T) != 5
+    assert np.abs(outs[0, keep] - ref[0, keep]).max() <= 1e-4
+    assert np.isfinite(to64(S)[0, 0]).all()
+    for h in (1, 2):
+        assert np.abs(outs[h, :5] - ref[h, :5]).max() <= 1e-4
+        assert not np.isfinite(outs[h, 5:]).all(axis=-1).any()
+        assert not np.isfinite(to64(S)[0, h]).all()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
