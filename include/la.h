@@ -155,6 +155,26 @@ la_status la_fwd_causal_decay(const void *q, const void *k, const void *v, void 
                               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Causal forward that allocates nothing, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, result and errors as la_fwd_causal, without
+ * the workspace: the per-segment states live in a device array the library
+ * owns, LA_NOALLOC_SCRATCH_BYTES per GPU, held from load until the process
+ * ends.  The split of each sequence into segments is capped so that its states
+ * fit the array (at one segment per (b, h) none are stored, so no size is
+ * refused for lack of room; large d_k x d_v problems may run fewer segments
+ * than la_fwd_causal and round differently within the usual tolerance).
+ * Calls share their GPU's array: calls that overlap on one GPU (other streams
+ * or host threads) race and must be serialised by the caller.  The first call
+ * on a device looks up the array's address there (hipGetSymbolAddress) and
+ * can fail with LA_ERR_LAUNCH.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+la_status la_fwd_causal_noalloc(const void *q, const void *k, const void *v, void *o, float *den,
+                                int B, int H, int N, int d_k, int d_v, int C,
+                                la_dtype in, la_dtype out, hipStream_t stream);
+
+/*
  * Causal backward by cumulative sums: the exact gradient of la_fwd_causal
  * with respect to q, k and v for an upstream gradient dO.
  * With g_i = dO_i, den_i = phi(q_i) . z_i, gh_i = g_i / den_i and

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     la_fwd_causal,
     la_fwd_causal_state,
     la_fwd_causal_decay,
+    la_fwd_causal_noalloc,
     la_fwd_noncausal,
     la_bwd_causal,
     la_bwd_noncausal,

@@ -28,6 +28,7 @@ EXPORTS = (
     "la_fwd_causal",
     "la_fwd_causal_state",
     "la_fwd_causal_decay",
+    "la_fwd_causal_noalloc",
     "la_bwd_causal",
     "la_bwd_noncausal",
     "la_decode_step",
@@ -72,6 +73,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_fwd_causal_state.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_fwd_causal_decay.argtypes = [vp] * 10 + [i] * 8 + [vp, sz, vp]
     lib.la_fwd_causal_decay.restype = i
+    lib.la_fwd_causal_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    lib.la_fwd_causal_noalloc.restype = i
     lib.la_fwd_causal_state.restype = i
     lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_causal.restype = i

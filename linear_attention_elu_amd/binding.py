@@ -161,6 +161,22 @@ def la_fwd_causal(q, k, v, o=None, den=None, C: int = 64, out_dtype=None, ws=Non
     return o, den
 
 
+def la_fwd_causal_noalloc(q, k, v, o, den=None, C: int = 64, stream=None):
+    """Causal forward into caller-given o (and den), with no workspace: the
+    library's own device array holds the segment states.  Allocates nothing.
+    Returns (o, den)."""
+    B, H, N, dk, dv = _shapes(q, k, v)
+    dev = _dev(q, k, v, o, den)
+    if tuple(o.shape) != (B, H, N, dv) or (den is not None and tuple(den.shape) != (B, H, N)):
+        raise ValueError("o must be [B,H,N,d_v] and den [B,H,N]")
+    if den is not None and den.dtype != torch.float32:
+        raise TypeError("den is float32")
+    rc = _lib.load().la_fwd_causal_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), B, H, N, dk, dv, C,
+                                           _code(q), _code(o), _stream(dev, stream))
+    _lib.check(rc, "la_fwd_causal_noalloc")
+    return o, den
+
+
 def la_fwd_noncausal(q, k, v, o=None, out_dtype=None, ws=None, stream=None):
     """Non-causal forward.  Returns o."""
     B, H, N, dk, dv = _shapes(q, k, v)

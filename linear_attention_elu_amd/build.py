@@ -23,6 +23,7 @@ SOURCES = [
     "la_decode.hip",
     "la_bwd.hip",
     "la_scan.hip",
+    "la_noalloc.hip",
     "la_fwd_dk16.hip",
     "la_fwd_dk32.hip",
     "la_fwd_dk64.hip",

@@ -42,7 +42,7 @@ long resident_workgroups(const void *kernel, OccCache &cache, int threads) {
 
 }  // namespace la
 
-namespace {
+namespace la {
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool chunk_ok(int C) { return C == 16 || C == 32 || C == 64; }
@@ -61,9 +61,9 @@ size_t fwd_ws_bytes(int B, int H, int N, int dk, int dv, int C, bool causal) {
     if (B < 1 || H < 1 || N < 1 || !dim_ok(dk) || !dim_ok(dv) || !chunk_ok(C)) return 0;
     const long BH = (long)B * H;
     int L = 0;
-    const int P = la::plan_segments(BH, N, C, la::kMaxTargetWg, &L);
+    const int P = plan_segments(BH, N, C, kMaxTargetWg, &L);
     if (causal && P == 1) return 0;
-    return (size_t)BH * P * la::state_floats(dk, dv) * sizeof(float);
+    return (size_t)BH * P * state_floats(dk, dv) * sizeof(float);
 }
 
 la_status from_hip(hipError_t e) {
@@ -72,18 +72,48 @@ la_status from_hip(hipError_t e) {
     return LA_ERR_LAUNCH;
 }
 
-// Chunk size the non-causal path tiles its sequence with (not part of its ABI).
-constexpr int kNonCausalChunk = 64;
+la_status check_fwd_causal_args(const void *q, const void *k, const void *v, const void *o, const void *den,
+                                const void *S0, const void *z0, const void *S_out, const void *z_out, int B,
+                                int H, int N, int d_k, int d_v, int C, int in, int out) {
+    if (!q || !k || !v || !o) return LA_ERR_NULL_PTR;
+    if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL_PTR;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL_PTR;
+    la_status st = check_shape(B, H, N);
+    if (st != LA_OK) return st;
+    if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return LA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in) || !dtype_ok(out)) return LA_ERR_BAD_DTYPE;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned_or_null(den) ||
+        !aligned_or_null(S0) || !aligned_or_null(z0) || !aligned_or_null(S_out) || !aligned_or_null(z_out))
+        return LA_ERR_ALIGNMENT;
+    return LA_OK;
+}
 
-la_status run_fwd(const la::FwdDesc &d, bool causal) {
+la_status run_fwd(const FwdDesc &d, bool causal) {
     switch (d.DK) {
-        case 16: return from_hip(la::run_fwd_dk16(d, causal));
-        case 32: return from_hip(la::run_fwd_dk32(d, causal));
-        case 64: return from_hip(la::run_fwd_dk64(d, causal));
-        case 128: return from_hip(la::run_fwd_dk128(d, causal));
+        case 16: return from_hip(run_fwd_dk16(d, causal));
+        case 32: return from_hip(run_fwd_dk32(d, causal));
+        case 64: return from_hip(run_fwd_dk64(d, causal));
+        case 128: return from_hip(run_fwd_dk128(d, causal));
         default: return LA_ERR_UNSUPPORTED;
     }
 }
+
+}  // namespace la
+
+namespace {
+
+using la::aligned;
+using la::aligned_or_null;
+using la::check_shape;
+using la::chunk_ok;
+using la::dim_ok;
+using la::dtype_ok;
+using la::from_hip;
+using la::fwd_ws_bytes;
+using la::run_fwd;
+
+// Chunk size the non-causal path tiles its sequence with (not part of its ABI).
+constexpr int kNonCausalChunk = 64;
 
 }  // namespace
 
@@ -126,17 +156,9 @@ la_status la_fwd_causal_decay(const void *q, const void *k, const void *v, void 
                               int B, int H, int N, int d_k, int d_v, int C,
                               la_dtype in, la_dtype out,
                               void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (!q || !k || !v || !o) return LA_ERR_NULL_PTR;
-    if ((S0 == nullptr) != (z0 == nullptr)) return LA_ERR_NULL_PTR;
-    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_NULL_PTR;
-    la_status st = check_shape(B, H, N);
+    la_status st = la::check_fwd_causal_args(q, k, v, o, den, S0, z0, S_out, z_out, B, H, N, d_k, d_v, C, in, out);
     if (st != LA_OK) return st;
-    if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return LA_ERR_UNSUPPORTED;
-    if (!dtype_ok(in) || !dtype_ok(out)) return LA_ERR_BAD_DTYPE;
-    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(o) || !aligned_or_null(den) ||
-        !aligned_or_null(S0) || !aligned_or_null(z0) || !aligned_or_null(S_out) || !aligned_or_null(z_out) ||
-        !aligned_or_null(ws))
-        return LA_ERR_ALIGNMENT;
+    if (!aligned_or_null(ws)) return LA_ERR_ALIGNMENT;
     const size_t need = fwd_ws_bytes(B, H, N, d_k, d_v, C, true);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return LA_ERR_WORKSPACE;
     la::FwdDesc d{q, k, v, o, den, S0, z0, S_out, z_out, B, H, N, d_k, d_v, C,

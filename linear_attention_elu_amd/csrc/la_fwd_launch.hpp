@@ -34,7 +34,14 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
                               : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
-    const long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY>();
+    long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY>();
+    // A workspace holding at most d.ws_states segment states (a fixed scratch):
+    // fewer segments per (b, h), down to one, which stores no state at all.
+    if (causal && d.ws_states > 0) {
+        const long per_bh = d.ws_states / BH;
+        const long cap = per_bh >= 1 ? per_bh * BH : BH;
+        if (cap < target_agg) target_agg = cap;
+    }
     const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>()
                                     : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF>();
     int Lf = 0;

@@ -7,6 +7,8 @@
 
 #include <atomic>
 
+#include "la.h"
+
 namespace la {
 
 struct FwdDesc {
@@ -20,6 +22,7 @@ struct FwdDesc {
     float *ws;
     hipStream_t stream;
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
+    long ws_states;      // causal only: if > 0, at most this many segment states fit the workspace
 };
 
 struct DecodeDesc {
@@ -75,6 +78,14 @@ inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
                            int mode, int lim, hipStream_t stream, const float *gamma = nullptr, int H = 1,
                            int L = 0);
+
+// Argument checks of the causal forward entry points (all but the workspace),
+// before any HIP call; the status the entry point returns.
+la_status check_fwd_causal_args(const void *q, const void *k, const void *v, const void *o, const void *den,
+                                const void *S0, const void *z0, const void *S_out, const void *z_out, int B,
+                                int H, int N, int d_k, int d_v, int C, int in, int out);
+// Dispatch of a checked forward by d_k; launch errors map to LA_ERR_LAUNCH.
+la_status run_fwd(const FwdDesc &d, bool causal);
 
 hipError_t run_fwd_dk16(const FwdDesc &d, bool causal);
 hipError_t run_fwd_dk32(const FwdDesc &d, bool causal);

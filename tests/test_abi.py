@@ -181,6 +181,29 @@ def test_fwd_causal_decay_rejects(lib):
     assert f(*bad) == 7
 
 
+def test_fwd_causal_noalloc_rejects(lib):
+    f = lib.la_fwd_causal_noalloc
+    args = [P] * 4 + [None] + [1, 1, 64, 64, 64, 64, 1, 1, None]
+    bad = list(args)
+    bad[0] = None  # q
+    assert f(*bad) == 1
+    bad = list(args)
+    bad[7] = 0  # N
+    assert f(*bad) == 2
+    bad = list(args)
+    bad[8] = 24  # d_k
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[10] = 128  # C
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[12] = 3  # out dtype
+    assert f(*bad) == 4
+    bad = list(args)
+    bad[4] = MIS  # den
+    assert f(*bad) == 7
+
+
 def test_decode_decay_rejects(lib):
     f = lib.la_decode_step_decay
     assert f(P, P, P, P, P, P, None, 1, 1, 32, 32, 0, None) == 1
