@@ -14,9 +14,10 @@ resident in HBM.  Alongside it, on the same JSON line:
                 (pixel-by-pixel generation of 32x32x3 images), replayed as one
                 HIP graph: steps/s and algorithmic bytes (state read and written,
                 q, k, v read, o written) against 8 TB/s;
-  extra         the length sweep N = 2^9 .. 2^16, the non-causal workload
-                (B=4, H=8, N=4096, d=64) and, when built, the backward
-                (B=8, H=16, N=8192, d=128, C=64);
+  extra         the length sweep N = 2^9 .. 2^16 (forward and backward time,
+                peak device bytes per call), the non-causal workload
+                (B=4, H=8, N=4096, d=64), the forward and backward at
+                B=8, H=16, N=8192, d=128, C=64, and the decay forward;
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a bounded sample
                 of the headline workload.
 Inputs are seeded synthetic normals.  One GPU only.
@@ -121,6 +122,51 @@ def bench_fwd(steps, warmup, dev, B=8, H=8, N=65536, d=64, C=64, seed=0):
         "ms": ms, "tokens_per_s": B * N / (ms * 1e-3), "bytes": bytes_alg, "flops": flops_alg,
         "gbs": bytes_alg / (ms * 1e-3) / 1e9, "tflops": flops_alg / (ms * 1e-3) / 1e12,
     }
+
+
+def bench_sweep_point(dev, N, steps, warmup, B=8, H=8, d=64, C=64, seed=0):
+    """One length of the sweep 2^9 .. 2^16 (velog review 4.3 times the forward and
+    the backward and reports peak memory at each length): forward and backward
+    time, and the device bytes resident during each call -- inputs, outputs and
+    workspace; the allocator's peak over the timed calls is checked to equal
+    them (the library allocates nothing)."""
+    import torch
+
+    import linear_attention_elu_amd as la
+    from linear_attention_elu_amd import inputs
+
+    stream = torch.cuda.current_stream(dev)
+
+    def resident_during(fn, base):
+        torch.cuda.synchronize()
+        held = torch.cuda.memory_allocated(dev) - base
+        torch.cuda.reset_peak_memory_stats(dev)
+        ms = time_calls(fn, steps, warmup, stream)
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        assert peak == held, (peak, held)
+        return ms, held
+
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    host = inputs.attention_inputs(B, H, N, d, d, seed=seed, with_grad=True)
+    q, k, v = (inputs.to_torch(host[n], torch.bfloat16, dev) for n in ("q", "k", "v"))
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, la.la_fwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
+    ms, fwd_bytes = resident_during(lambda: la.la_fwd_causal(q, k, v, o=o, C=C, ws=ws, want_den=False), base)
+    del o, ws
+    dO = inputs.to_torch(host["dO"], torch.bfloat16, dev)
+    del host
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    wsb = torch.empty(max(1, la.la_bwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
+    bms, bwd_bytes = resident_during(lambda: la.la_bwd_causal(q, k, v, dO, dq=dq, dk=dk, dv=dv, C=C, ws=wsb), base)
+    th = B * H * N
+    fby, bby = th * 4 * d * 2, th * 7 * d * 2
+    flops = th * (4 * C * d + 4 * d * d)
+    return {"us": round(ms * 1e3, 2), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+            "hbm_frac": round(fby / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "bwd_us": round(bms * 1e3, 2), "bwd_hbm_frac": round(bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_device_bytes": int(fwd_bytes), "bwd_device_bytes": int(bwd_bytes)}
 
 
 def bench_fwd_decay(steps, warmup, dev, B=8, H=8, N=65536, d=64, C=64, seed=0):
@@ -403,11 +449,7 @@ def main():
         log("extra: length sweep, non-causal, fwd+bwd")
         sweep = {}
         for e in range(9, 17):
-            N = 2 ** e
-            s = bench_fwd(max(5, args.steps), 20, dev, N=N)
-            sweep[str(N)] = {"us": round(s["ms"] * 1e3, 2), "tokens_per_s": round(s["tokens_per_s"], 1),
-                             "hbm_frac": round(s["gbs"] / HBM_PEAK_GBS, 4),
-                             "mfma_frac": round(s["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}
+            sweep[str(2 ** e)] = bench_sweep_point(dev, 2 ** e, max(5, args.steps), 20)
         res["extra"] = {"causal_sweep_B8_H8_d64_C64": sweep, "noncausal": bench_noncausal(dev),
                         "fwd_bwd": bench_bwd(dev), "causal_decay": bench_fwd_decay(args.steps, args.warmup, dev)}
     if not args.no_cpu_baseline:
