@@ -14,6 +14,12 @@ from .oracle import (  # noqa: F401
     fwd_causal_decay,
     decode_step_decay,
     bwd_causal_decay,
+    FEATURE_MAPS,
+    features,
+    fwd_causal_fm,
+    fwd_noncausal_fm,
+    decode_step_fm,
+    bwd_causal_fm,
     num_threads,
     library_path,
     load_variant,

@@ -524,3 +524,260 @@ void oracle_bwd_causal_decay_f64(const double *q, const double *k, const double 
         free(Sp);
     }
 }
+
+/*
+ * ---------------------------------------------------------------------------
+ * Pluggable feature map (itwiki "선형 어텐션", section "특징 사상 선택"
+ * (choice of feature map), which lists elu + 1, Performer's positive
+ * orthogonal random features and the identity; blog digest "Digest" (open
+ * questions: better feature maps such as Performer's random features)).
+ *
+ * kind 0, elu + 1:  phi(x) = elu(x) + 1 as above, m = dk.
+ * kind 1, identity: phi(x) = x, m = dk (the caller supplies features that
+ *                   keep the denominators positive).
+ * kind 2, positive random features approximating the softmax kernel
+ *                   exp(q . k) without bias:
+ *                   phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m),  r < m,
+ *                   with w_r the r-th of m random directions of dimension dk,
+ *                   W[h][r][e] for head h (drawn by the caller).
+ *                   Then E_w[phi(q) . phi(k)] = exp(q . k) for w ~ N(0, I).
+ * The attention itself is unchanged: the state has m rows instead of dk.
+ * ---------------------------------------------------------------------------
+ */
+static void fm_feature(int kind, const double *Wh, int m, const double *x, int dk, double *out)
+{
+    if (kind == 0) {
+        for (int e = 0; e < dk; ++e) out[e] = phi(x[e]);
+    } else if (kind == 1) {
+        for (int e = 0; e < dk; ++e) out[e] = x[e];
+    } else {
+        double nx = 0.0;
+        for (int e = 0; e < dk; ++e) nx += x[e] * x[e];
+        for (int r = 0; r < m; ++r) {
+            double a = 0.0;
+            for (int e = 0; e < dk; ++e) a += Wh[(long)r * dk + e] * x[e];
+            out[r] = exp(a - 0.5 * nx) / sqrt((double)m);
+        }
+    }
+}
+
+/* dx = J^T dphi, J the Jacobian of the feature map at x:
+ * elu + 1: diag(phi'(x)); identity: I; random features:
+ * d phi_r / d x_e = phi_r(x) (w_re - x_e). */
+static void fm_feature_vjp(int kind, const double *Wh, int m, const double *x, int dk, const double *dphi_in,
+                           double *dx)
+{
+    if (kind == 0) {
+        for (int e = 0; e < dk; ++e) dx[e] = dphi_in[e] * dphi(x[e]);
+    } else if (kind == 1) {
+        for (int e = 0; e < dk; ++e) dx[e] = dphi_in[e];
+    } else {
+        double *f = malloc((size_t)m * sizeof(double));
+        fm_feature(kind, Wh, m, x, dk, f);
+        for (int e = 0; e < dk; ++e) dx[e] = 0.0;
+        for (int r = 0; r < m; ++r) {
+            double u = dphi_in[r] * f[r];
+            for (int e = 0; e < dk; ++e) dx[e] += u * (Wh[(long)r * dk + e] - x[e]);
+        }
+        free(f);
+    }
+}
+
+/* Feature dimension of a map (m for random features, dk otherwise). */
+static int fm_dim(int kind, int m, int dk) { return kind == 2 ? m : dk; }
+
+/* The feature map alone: phi of every row of x [B][H][N][dk] into out [B][H][N][m']. */
+void oracle_fm_features_f64(const double *x, int kind, const double *W, int m, double *out,
+                            int B, int H, int N, int dk)
+{
+    long BH = (long)B * H;
+    int mf = fm_dim(kind, m, dk);
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *Wh = kind == 2 ? W + (bh % H) * (long)m * dk : NULL;
+        for (int i = 0; i < N; ++i)
+            fm_feature(kind, Wh, m, x + (bh * N + i) * (long)dk, dk, out + (bh * N + i) * (long)mf);
+    }
+}
+
+/* Causal forward with a feature map: the recurrent form of
+ * oracle_fwd_causal_f64 with phi replaced by the map (state S [m'][dv]). */
+void oracle_fwd_causal_fm_f64(const double *q, const double *k, const double *v, int kind, const double *W,
+                              int m, double *o, double *den, int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int mf = fm_dim(kind, m, dk);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *Wh = kind == 2 ? W + (bh % H) * (long)m * dk : NULL;
+        double *S = calloc((size_t)mf * dv, sizeof(double));
+        double *z = calloc((size_t)mf, sizeof(double));
+        double *fq = malloc((size_t)mf * sizeof(double));
+        double *fk = malloc((size_t)mf * sizeof(double));
+        for (int i = 0; i < N; ++i) {
+            const double *vi = v + (bh * N + i) * (long)dv;
+            fm_feature(kind, Wh, m, k + (bh * N + i) * (long)dk, dk, fk);
+            for (int e = 0; e < mf; ++e) {
+                z[e] += fk[e];
+                for (int c = 0; c < dv; ++c) S[(long)e * dv + c] += fk[e] * vi[c];
+            }
+            fm_feature(kind, Wh, m, q + (bh * N + i) * (long)dk, dk, fq);
+            double d = 0.0;
+            for (int e = 0; e < mf; ++e) d += fq[e] * z[e];
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < mf; ++e) num += fq[e] * S[(long)e * dv + c];
+                o[(bh * N + i) * (long)dv + c] = num / d;
+            }
+            if (den) den[bh * (long)N + i] = d;
+        }
+        free(S);
+        free(z);
+        free(fq);
+        free(fk);
+    }
+}
+
+/* Non-causal forward with a feature map (sums over all N tokens). */
+void oracle_fwd_noncausal_fm_f64(const double *q, const double *k, const double *v, int kind, const double *W,
+                                 int m, double *o, int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int mf = fm_dim(kind, m, dk);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *Wh = kind == 2 ? W + (bh % H) * (long)m * dk : NULL;
+        double *S = calloc((size_t)mf * dv, sizeof(double));
+        double *z = calloc((size_t)mf, sizeof(double));
+        double *f = malloc((size_t)mf * sizeof(double));
+        for (int j = 0; j < N; ++j) {
+            fm_feature(kind, Wh, m, k + (bh * N + j) * (long)dk, dk, f);
+            for (int e = 0; e < mf; ++e) {
+                z[e] += f[e];
+                for (int c = 0; c < dv; ++c) S[(long)e * dv + c] += f[e] * v[(bh * N + j) * (long)dv + c];
+            }
+        }
+        for (int i = 0; i < N; ++i) {
+            fm_feature(kind, Wh, m, q + (bh * N + i) * (long)dk, dk, f);
+            double d = 0.0;
+            for (int e = 0; e < mf; ++e) d += f[e] * z[e];
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < mf; ++e) num += f[e] * S[(long)e * dv + c];
+                o[(bh * N + i) * (long)dv + c] = num / d;
+            }
+        }
+        free(S);
+        free(z);
+        free(f);
+    }
+}
+
+/* One decode step with a feature map: S [B][H][m'][dv], z [B][H][m'] in place. */
+void oracle_decode_step_fm_f64(double *S, double *z, const double *q, const double *k, const double *v, int kind,
+                               const double *W, int m, double *o, int B, int H, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int mf = fm_dim(kind, m, dk);
+#pragma omp parallel for schedule(static)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *Wh = kind == 2 ? W + (bh % H) * (long)m * dk : NULL;
+        double *Sb = S + bh * (long)mf * dv;
+        double *zb = z + bh * (long)mf;
+        double *fq = malloc((size_t)mf * sizeof(double));
+        double *fk = malloc((size_t)mf * sizeof(double));
+        fm_feature(kind, Wh, m, k + bh * (long)dk, dk, fk);
+        fm_feature(kind, Wh, m, q + bh * (long)dk, dk, fq);
+        for (int e = 0; e < mf; ++e) {
+            zb[e] += fk[e];
+            for (int c = 0; c < dv; ++c) Sb[(long)e * dv + c] += fk[e] * v[bh * (long)dv + c];
+        }
+        double d = 0.0;
+        for (int e = 0; e < mf; ++e) d += fq[e] * zb[e];
+        for (int c = 0; c < dv; ++c) {
+            double num = 0.0;
+            for (int e = 0; e < mf; ++e) num += fq[e] * Sb[(long)e * dv + c];
+            o[bh * (long)dv + c] = num / d;
+        }
+        free(fq);
+        free(fk);
+    }
+}
+
+/*
+ * Gradient of the causal form with a feature map: the cumulative-sum gradient
+ * of oracle_bwd_causal_f64 taken with respect to the features, phi_q = phi(q_i)
+ * and phi_k = phi(k_j), then carried back through the map (fm_feature_vjp).
+ */
+void oracle_bwd_causal_fm_f64(const double *q, const double *k, const double *v, const double *g, int kind,
+                              const double *W, int m, double *dq, double *dk_out, double *dv_out,
+                              int B, int H, int N, int dk, int dv)
+{
+    long BH = (long)B * H;
+    int dv1 = dv + 1;
+    int mf = fm_dim(kind, m, dk);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const double *Wh = kind == 2 ? W + (bh % H) * (long)m * dk : NULL;
+        const double *qb = q + bh * (long)N * dk;
+        const double *kb = k + bh * (long)N * dk;
+        const double *vb = v + bh * (long)N * dv;
+        const double *gb = g + bh * (long)N * dv;
+        double *FQ = malloc((size_t)N * mf * sizeof(double));
+        double *FK = malloc((size_t)N * mf * sizeof(double));
+        double *Gp = malloc((size_t)N * dv1 * sizeof(double));
+        double *Sp = calloc((size_t)mf * dv1, sizeof(double));
+        double *df = malloc((size_t)mf * sizeof(double));
+        for (int i = 0; i < N; ++i) {
+            fm_feature(kind, Wh, m, qb + (long)i * dk, dk, FQ + (long)i * mf);
+            fm_feature(kind, Wh, m, kb + (long)i * dk, dk, FK + (long)i * mf);
+        }
+        /* Forward sweep: S'_i, out_i and den_i, G'_i, then dphi_q(i) = S'_i G'_i. */
+        for (int i = 0; i < N; ++i) {
+            const double *fk = FK + (long)i * mf, *fq = FQ + (long)i * mf;
+            for (int e = 0; e < mf; ++e) {
+                for (int c = 0; c < dv; ++c) Sp[(long)e * dv1 + c] += fk[e] * vb[(long)i * dv + c];
+                Sp[(long)e * dv1 + dv] += fk[e];
+            }
+            double d = 0.0;
+            for (int e = 0; e < mf; ++e) d += fq[e] * Sp[(long)e * dv1 + dv];
+            double go = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int e = 0; e < mf; ++e) num += fq[e] * Sp[(long)e * dv1 + c];
+                go += gb[(long)i * dv + c] * (num / d);
+                Gp[(long)i * dv1 + c] = gb[(long)i * dv + c] / d;
+            }
+            Gp[(long)i * dv1 + dv] = -go / d;
+            for (int e = 0; e < mf; ++e) {
+                double acc = 0.0;
+                for (int c = 0; c < dv1; ++c) acc += Sp[(long)e * dv1 + c] * Gp[(long)i * dv1 + c];
+                df[e] = acc;
+            }
+            fm_feature_vjp(kind, Wh, m, qb + (long)i * dk, dk, df, dq + (bh * N + i) * (long)dk);
+        }
+        /* Reverse sweep: R'_j, then dphi_k(j) = R'_j V'_j and dv_j = R_j^T phi_k(j). */
+        memset(Sp, 0, (size_t)mf * dv1 * sizeof(double));
+        for (int j = N - 1; j >= 0; --j) {
+            const double *fk = FK + (long)j * mf, *fq = FQ + (long)j * mf;
+            for (int e = 0; e < mf; ++e)
+                for (int c = 0; c < dv1; ++c) Sp[(long)e * dv1 + c] += fq[e] * Gp[(long)j * dv1 + c];
+            for (int e = 0; e < mf; ++e) {
+                double acc = Sp[(long)e * dv1 + dv];
+                for (int c = 0; c < dv; ++c) acc += Sp[(long)e * dv1 + c] * vb[(long)j * dv + c];
+                df[e] = acc;
+            }
+            fm_feature_vjp(kind, Wh, m, kb + (long)j * dk, dk, df, dk_out + (bh * N + j) * (long)dk);
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int e = 0; e < mf; ++e) acc += Sp[(long)e * dv1 + c] * fk[e];
+                dv_out[(bh * N + j) * (long)dv + c] = acc;
+            }
+        }
+        free(FQ);
+        free(FK);
+        free(Gp);
+        free(Sp);
+        free(df);
+    }
+}

@@ -46,6 +46,11 @@ def _bind(path: str):
     lib.oracle_fwd_causal_decay_f64.argtypes = [P, P, P, P, P, P, i, i, i, i, i]
     lib.oracle_decode_step_decay_f64.argtypes = [P, P, P, P, P, P, P, i, i, i, i]
     lib.oracle_bwd_causal_decay_f64.argtypes = [P, P, P, P, P, P, P, P, i, i, i, i, i]
+    lib.oracle_fm_features_f64.argtypes = [P, i, P, i, P, i, i, i, i]
+    lib.oracle_fwd_causal_fm_f64.argtypes = [P, P, P, i, P, i, P, P, i, i, i, i, i]
+    lib.oracle_fwd_noncausal_fm_f64.argtypes = [P, P, P, i, P, i, P, i, i, i, i, i]
+    lib.oracle_decode_step_fm_f64.argtypes = [P, P, P, P, P, i, P, i, P, i, i, i, i]
+    lib.oracle_bwd_causal_fm_f64.argtypes = [P, P, P, P, i, P, i, P, P, P, i, i, i, i, i]
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
@@ -193,3 +198,83 @@ def load_variant(path: str):
 
 def source_path() -> str:
     return _SRC
+
+
+# ---------------------------------------------------------------------------
+# Pluggable feature map: "elu1" (phi = elu + 1), "identity" (phi(x) = x) and
+# "prf" (positive random features phi(x)_r = exp(w_r . x - |x|^2/2) / sqrt(m),
+# W [H, m, d_k], one set of m directions per head).
+# ---------------------------------------------------------------------------
+FEATURE_MAPS = {"elu1": 0, "identity": 1, "prf": 2}
+
+
+def _fm(kind, W, H, dk):
+    code = FEATURE_MAPS[kind]
+    if code == 2:
+        W = _f64(W)
+        assert W.ndim == 3 and W.shape[0] == H and W.shape[2] == dk, W.shape
+        return code, W, W.shape[1]
+    return code, np.zeros(1), dk
+
+
+def features(x, kind, W=None, lib=None):
+    """The feature map of every row of x [B,H,N,dk] -> [B,H,N,m]."""
+    x = _f64(x)
+    B, H, N, dk = x.shape
+    code, Wa, m = _fm(kind, W, H, dk)
+    out = np.empty((B, H, N, m))
+    (lib or _load()).oracle_fm_features_f64(_ptr(x), code, _ptr(Wa), m, _ptr(out), B, H, N, dk)
+    return out
+
+
+def fwd_causal_fm(q, k, v, kind, W=None, lib=None):
+    """Causal forward with a feature map: (out [B,H,N,dv], den [B,H,N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    code, Wa, m = _fm(kind, W, H, dk)
+    o = np.empty((B, H, N, dv))
+    den = np.empty((B, H, N))
+    (lib or _load()).oracle_fwd_causal_fm_f64(_ptr(q), _ptr(k), _ptr(v), code, _ptr(Wa), m, _ptr(o), _ptr(den),
+                                             B, H, N, dk, dv)
+    return o, den
+
+
+def fwd_noncausal_fm(q, k, v, kind, W=None, lib=None):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    code, Wa, m = _fm(kind, W, H, dk)
+    o = np.empty((B, H, N, dv))
+    (lib or _load()).oracle_fwd_noncausal_fm_f64(_ptr(q), _ptr(k), _ptr(v), code, _ptr(Wa), m, _ptr(o),
+                                                B, H, N, dk, dv)
+    return o
+
+
+def decode_step_fm(S, z, q, k, v, kind, W=None, lib=None):
+    """One decode step with a feature map.  S: [B,H,m,dv], z: [B,H,m]; returns (S, z, out)."""
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    code, Wa, m = _fm(kind, W, H, dk)
+    assert S.shape == (B, H, m, dv) and z.shape == (B, H, m)
+    o = np.empty((B, H, dv))
+    (lib or _load()).oracle_decode_step_fm_f64(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), code, _ptr(Wa), m,
+                                              _ptr(o), B, H, dk, dv)
+    return S, z, o
+
+
+def bwd_causal_fm(q, k, v, dout, kind, W=None, lib=None):
+    """Exact gradient of the causal forward with a feature map: (dq, dk, dv)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, dk = q.shape
+    dv = v.shape[-1]
+    code, Wa, m = _fm(kind, W, H, dk)
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    (lib or _load()).oracle_bwd_causal_fm_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), code, _ptr(Wa), m, _ptr(dq),
+                                             _ptr(dkk), _ptr(dvv), B, H, N, dk, dv)
+    return dq, dkk, dvv

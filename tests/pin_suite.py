@@ -272,9 +272,120 @@ def check_backward_decay(lib=None):
     np.testing.assert_allclose(z0[2], g, rtol=1e-13, atol=1e-14)
 
 
+def check_random_features(lib=None):
+    """Positive random features (itwiki '선형 어텐션', section '특징 사상 선택': an
+    unbiased estimate of the softmax kernel exp(q . k)).  Closed forms: with all
+    directions zero every feature is exp(-|x|^2/2)/sqrt(m), so phi(q).phi(k) =
+    exp(-(|q|^2 + |k|^2)/2); with one direction w, phi(q)phi(k) =
+    exp(w.(q + k) - (|q|^2 + |k|^2)/2).  The defining property: averaged over
+    w ~ N(0, I), phi(q).phi(k) = exp(q . k), with an error that shrinks like
+    1/sqrt(m)."""
+    r = _rng(51)
+    q = r.standard_normal((1, 2, 3, 8)) * 0.4
+    k = r.standard_normal((1, 2, 3, 8)) * 0.4
+    for m in (16, 64):
+        fq = oracle.features(q, "prf", np.zeros((2, m, 8)), lib=lib)
+        fk = oracle.features(k, "prf", np.zeros((2, m, 8)), lib=lib)
+        want = np.exp(-0.5 * ((q ** 2).sum(-1)[..., :, None] + (k ** 2).sum(-1)[..., None, :]))
+        np.testing.assert_allclose(fq @ np.swapaxes(fk, -1, -2), want, rtol=1e-13)
+    w = r.standard_normal((2, 1, 8))
+    fq = oracle.features(q, "prf", w, lib=lib)[..., 0]
+    fk = oracle.features(k, "prf", w, lib=lib)[..., 0]
+    wq = np.einsum("bhne,he->bhn", q, w[:, 0])
+    wk = np.einsum("bhne,he->bhn", k, w[:, 0])
+    np.testing.assert_allclose(fq, np.exp(wq - 0.5 * (q ** 2).sum(-1)), rtol=1e-13)
+    np.testing.assert_allclose(fk, np.exp(wk - 0.5 * (k ** 2).sum(-1)), rtol=1e-13)
+    # unbiasedness: 24 (q, k) pairs, directions N(0, I); mean relative error at
+    # m = 256 and m = 16384 (64x more features -> about 8x smaller error)
+    dk = 6
+    qs = r.standard_normal((24, dk)) * 0.35
+    ks = r.standard_normal((24, dk)) * 0.35
+    errs = []
+    for m in (256, 16384):
+        W = r.standard_normal((1, m, dk))
+        fq = oracle.features(qs[None, None], "prf", W, lib=lib)[0, 0]
+        fk = oracle.features(ks[None, None], "prf", W, lib=lib)[0, 0]
+        est = (fq * fk).sum(-1)
+        exact = np.exp((qs * ks).sum(-1))
+        terms = m * fq * fk                      # est is the mean of these m samples
+        se = terms.std(-1) / np.sqrt(m)
+        assert np.all(np.abs(est - exact) <= 5 * se), "estimate outside 5 standard errors"
+        errs.append(np.abs(est / exact - 1).mean())
+    assert 3.0 < errs[0] / errs[1] < 25.0, errs
+
+
+def check_feature_map_attention(lib=None):
+    """The attention with a feature map: elu + 1 through the map equals the plain
+    oracle; the identity map fed with phi(q), phi(k) equals it too; random
+    features give the masked quadratic form built on the same features (causal)
+    and the associative form (non-causal); T decode steps reproduce the causal
+    forward."""
+    q, k, v = _qkv(2, 2, 30, 8, 5, seed=52)
+    oc, dc = oracle.fwd_causal(q, k, v, lib=lib)
+    o1, d1 = oracle.fwd_causal_fm(q, k, v, "elu1", lib=lib)
+    np.testing.assert_array_equal(o1, oc)
+    np.testing.assert_array_equal(d1, dc)
+    o2, _ = oracle.fwd_causal_fm(forms.phi(q), forms.phi(k), v, "identity", lib=lib)
+    np.testing.assert_allclose(o2, oc, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oracle.fwd_noncausal_fm(forms.phi(q), forms.phi(k), v, "identity", lib=lib),
+                               oracle.fwd_noncausal(q, k, v, lib=lib), rtol=1e-13, atol=1e-14)
+    W = _rng(53).standard_normal((2, 12, 8))
+    qs, ks = q * 0.3, k * 0.3
+    fq, fk = oracle.features(qs, "prf", W, lib=lib), oracle.features(ks, "prf", W, lib=lib)
+    a = (fq @ np.swapaxes(fk, -1, -2)) * np.tril(np.ones((30, 30)))
+    o3, d3 = oracle.fwd_causal_fm(qs, ks, v, "prf", W, lib=lib)
+    np.testing.assert_allclose(o3, (a @ v) / a.sum(-1, keepdims=True), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(d3, a.sum(-1), rtol=1e-12)
+    kv = np.swapaxes(fk, -1, -2) @ v
+    np.testing.assert_allclose(oracle.fwd_noncausal_fm(qs, ks, v, "prf", W, lib=lib),
+                               (fq @ kv) / (fq @ fk.sum(-2)[..., None]), rtol=1e-11, atol=1e-12)
+    S = np.zeros((2, 2, 12, 5))
+    z = np.zeros((2, 2, 12))
+    outs = []
+    for t in range(30):
+        S, z, ot = oracle.decode_step_fm(S, z, qs[:, :, t], ks[:, :, t], v[:, :, t], "prf", W, lib=lib)
+        outs.append(ot)
+    np.testing.assert_array_equal(np.stack(outs, 2), o3)
+
+
+def check_feature_map_backward(lib=None):
+    """Gradient with a feature map == central finite differences of the masked
+    quadratic form built on the oracle's features (random features, identity);
+    elu + 1 through the map equals the plain gradient; sum_j dv_j = sum_i dO_i."""
+    B, H, N, dk, dv, m = 1, 2, 7, 3, 4, 5
+    q, k, v = _qkv(B, H, N, dk, dv, seed=54, scale=0.5)
+    g = _rng(55).standard_normal(v.shape)
+    W = _rng(56).standard_normal((H, m, dk))
+    # identity: features with entries of both signs (so that a stray elu' would
+    # show), shifted to keep every denominator away from zero (min 0.24 here)
+    for kind, Wk, xq, xk in (("prf", W, q, k), ("identity", None, np.exp(q) - 0.6, np.exp(k) - 0.6)):
+        dq, dkk, dvv = oracle.bwd_causal_fm(xq, xk, v, g, kind, Wk, lib=lib)
+
+        def out(a, b, c):
+            fa, fb = oracle.features(a, kind, Wk, lib=lib), oracle.features(b, kind, Wk, lib=lib)
+            w = (fa @ np.swapaxes(fb, -1, -2)) * np.tril(np.ones((N, N)))
+            return (w @ c) / w.sum(-1, keepdims=True)
+
+        for got, which in ((dq, 0), (dkk, 1), (dvv, 2)):
+            args = [xq, xk, v]
+
+            def loss(x, which=which, args=args):
+                a = list(args)
+                a[which] = x
+                return float((out(*a) * g).sum())
+
+            ref = forms.fd_gradient(loss, args[which].copy())
+            err = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30)
+            assert err < 1e-6, f"{kind}: finite-difference mismatch {err:.3e}"
+        np.testing.assert_allclose(dvv.sum(2), g.sum(2), rtol=1e-12, atol=1e-12)
+    for a, b in zip(oracle.bwd_causal_fm(q, k, v, g, "elu1", lib=lib), oracle.bwd_causal(q, k, v, g, lib=lib)):
+        np.testing.assert_array_equal(a, b)
+
+
 ALL_CHECKS = [check_golden, check_causal_vs_quadratic, check_causal_vs_chunked, check_noncausal,
               check_invariants, check_decode, check_backward, check_backward_noncausal, check_decay,
-              check_backward_decay]
+              check_backward_decay, check_random_features, check_feature_map_attention,
+              check_feature_map_backward]
 
 
 def failing_checks(lib):

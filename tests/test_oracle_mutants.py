@@ -71,6 +71,17 @@ MUTANTS = {
                                "Sp[(long)e * dv1 + c] = Sp[(long)e * dv1 + c] + fq * Gp[(long)j * dv1 + c];"),
     "dbwd_z_undecayed": ("Sp[(long)e * dv1 + dv] = gm * Sp[(long)e * dv1 + dv] + fk;",
                          "Sp[(long)e * dv1 + dv] = Sp[(long)e * dv1 + dv] + fk;"),
+    "fm_drops_half_norm": ("out[r] = exp(a - 0.5 * nx) / sqrt((double)m);", "out[r] = exp(a) / sqrt((double)m);"),
+    "fm_normalised_by_m": ("out[r] = exp(a - 0.5 * nx) / sqrt((double)m);", "out[r] = exp(a - 0.5 * nx) / (double)m;"),
+    "fm_direction_sign": ("a += Wh[(long)r * dk + e] * x[e];", "a -= Wh[(long)r * dk + e] * x[e];"),
+    "fm_directions_transposed": ("a += Wh[(long)r * dk + e] * x[e];", "a += Wh[(long)(e % m) * dk + (r % dk)] * x[e];"),
+    "fm_vjp_drops_x": ("dx[e] += u * (Wh[(long)r * dk + e] - x[e]);", "dx[e] += u * Wh[(long)r * dk + e];"),
+    "fm_vjp_drops_phi": ("double u = dphi_in[r] * f[r];", "double u = dphi_in[r];"),
+    "fm_identity_vjp_elu": ("for (int e = 0; e < dk; ++e) dx[e] = dphi_in[e];",
+                            "for (int e = 0; e < dk; ++e) dx[e] = dphi_in[e] * dphi(x[e]);"),
+    "fm_causal_drops_z": ("for (int e = 0; e < mf; ++e) d += fq[e] * z[e];", "for (int e = 0; e < mf; ++e) d += fq[e];"),
+    "fm_bwd_dv_uses_q": ("for (int e = 0; e < mf; ++e) acc += Sp[(long)e * dv1 + c] * fk[e];",
+                         "for (int e = 0; e < mf; ++e) acc += Sp[(long)e * dv1 + c] * fq[e];"),
     "nbwd_eps_sign": ("Gi[dv] = -go / d;", "Gi[dv] = go / d;"),
     "nbwd_drops_ones_column": ("double acc = Rp[(long)e * dv1 + dv]; /* times V'_j[dv] = 1 */",
                                "double acc = 0.0;"),
