@@ -23,7 +23,10 @@
  *   - gradient as cumulative sums with linear memory: velog 3.5; blog digest
  *     "Methods" (last item);
  *   - fixed per-head decay of the state: itwiki, table of later variants,
- *     RetNet row (la_fwd_causal_decay, la_decode_step_decay).
+ *     RetNet row (la_fwd_causal_decay, la_decode_step_decay);
+ *   - choice of feature map (elu + 1, Performer's positive random features,
+ *     identity): itwiki section "특징 사상 선택"; blog digest "Digest"
+ *     (the *_fm entry points).
  *
  * Conventions shared by every entry point
  *   Layout    All tensors are dense, row-major and contiguous:
@@ -84,6 +87,23 @@ typedef enum {
 } la_status;
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Feature map phi of the *_fm entry points (itwiki "선형 어텐션", section
+ * "특징 사상 선택" (choice of feature map), which lists these three):
+ *   LA_PHI_ELU1      phi = elu + 1, as every other entry point (W, m unused);
+ *   LA_PHI_IDENTITY  phi(x) = x: q and k already are the features (W, m
+ *                    unused).  The normaliser phi(q) . sum phi(k) must stay
+ *                    away from zero; nothing checks it;
+ *   LA_PHI_PRF       Performer's positive random features, an unbiased
+ *                    estimate of the softmax kernel exp(q . k):
+ *                    phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), r < m,
+ *                    with W [H][m][d_k] in the input type holding m directions
+ *                    w_r per head (drawn by the caller, e.g. from N(0, I) in
+ *                    orthogonal blocks), d_k and m in {32, 64, 128}.  The
+ *                    features stay in fp32 range while |x|^2 / 2 - w_r . x
+ *                    stays below about 87.  The state then has m rows:
+ *                    S [B][H][m][d_v], z [B][H][m]. */
+typedef enum { LA_PHI_ELU1 = 0, LA_PHI_IDENTITY = 1, LA_PHI_PRF = 2 } la_feature_map;
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *la_status_string(la_status s);
@@ -213,6 +233,42 @@ la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const vo
                            void *dq, void *dk, void *dv,
                            int B, int H, int N, int d_k, int d_v, la_dtype in,
                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The causal forward, the non-causal forward, the causal backward and the
+ * decode step with a feature map (la_feature_map above).  Arguments, layouts
+ * and errors are those of the plain entry points, plus fm, W and m; the
+ * workspace queries take them and the input type too (the random map keeps
+ * phi(q), phi(k) -- and in the backward dphi(q), dphi(k) -- in the workspace
+ * as [B][H][N][m] in the input type).  Random features are computed on the
+ * matrix cores; the chunked kernels then run with the identity map over m
+ * features, and the backward carries dphi back through the map:
+ * dx = sum_r dphi_r phi_r(x) (w_r - x).  An unknown fm, or m or d_k outside
+ * {32, 64, 128} with LA_PHI_PRF, returns LA_ERR_UNSUPPORTED; a NULL W with
+ * LA_PHI_PRF returns LA_ERR_NULL_PTR.
+ */
+size_t la_fwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C,
+                                        la_feature_map fm, int m, la_dtype in);
+size_t la_fwd_noncausal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v,
+                                           la_feature_map fm, int m, la_dtype in);
+size_t la_bwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C,
+                                        la_feature_map fm, int m, la_dtype in);
+la_status la_fwd_causal_fm(const void *q, const void *k, const void *v, void *o, float *den,
+                           la_feature_map fm, const void *W, int m,
+                           int B, int H, int N, int d_k, int d_v, int C, la_dtype in, la_dtype out,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+la_status la_fwd_noncausal_fm(const void *q, const void *k, const void *v, void *o,
+                              la_feature_map fm, const void *W, int m,
+                              int B, int H, int N, int d_k, int d_v, la_dtype in, la_dtype out,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
+la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const void *dO,
+                           void *dq, void *dk, void *dv, la_feature_map fm, const void *W, int m,
+                           int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
+/* S [B][H][m'][d_v], z [B][H][m'] with m' = m for LA_PHI_PRF, d_k otherwise. */
+la_status la_decode_step_fm(float *S, float *z, const void *q, const void *k, const void *v, void *o,
+                            la_feature_map fm, const void *W, int m,
+                            int B, int H, int d_k, int d_v, la_dtype in, hipStream_t stream);
 
 /*
  * One recurrent decode step for every (b, h):

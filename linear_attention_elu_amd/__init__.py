@@ -19,4 +19,11 @@ from .binding import (  # noqa: F401
     la_bwd_noncausal,
     la_decode_step,
     la_decode_step_decay,
+    la_fwd_causal_fm_workspace_bytes,
+    la_fwd_noncausal_fm_workspace_bytes,
+    la_bwd_causal_fm_workspace_bytes,
+    la_fwd_causal_fm,
+    la_fwd_noncausal_fm,
+    la_bwd_causal_fm,
+    la_decode_step_fm,
 )

@@ -17,6 +17,10 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 LA_F32 = 0
 LA_BF16 = 1
 
+LA_PHI_ELU1 = 0
+LA_PHI_IDENTITY = 1
+LA_PHI_PRF = 2
+
 # Every symbol include/la.h declares.
 EXPORTS = (
     "la_status_string",
@@ -33,6 +37,13 @@ EXPORTS = (
     "la_bwd_noncausal",
     "la_decode_step",
     "la_decode_step_decay",
+    "la_fwd_causal_fm_workspace_bytes",
+    "la_fwd_noncausal_fm_workspace_bytes",
+    "la_bwd_causal_fm_workspace_bytes",
+    "la_fwd_causal_fm",
+    "la_fwd_noncausal_fm",
+    "la_bwd_causal_fm",
+    "la_decode_step_fm",
 )
 
 _lib = None
@@ -86,6 +97,20 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_decode_step_decay.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.la_decode_step_decay.restype = i
     lib.la_decode_step.restype = i
+    lib.la_fwd_causal_fm_workspace_bytes.argtypes = [i] * 9
+    lib.la_fwd_causal_fm_workspace_bytes.restype = sz
+    lib.la_fwd_noncausal_fm_workspace_bytes.argtypes = [i] * 8
+    lib.la_fwd_noncausal_fm_workspace_bytes.restype = sz
+    lib.la_bwd_causal_fm_workspace_bytes.argtypes = [i] * 9
+    lib.la_bwd_causal_fm_workspace_bytes.restype = sz
+    lib.la_fwd_causal_fm.argtypes = [vp] * 5 + [i, vp] + [i] * 9 + [vp, sz, vp]
+    lib.la_fwd_causal_fm.restype = i
+    lib.la_fwd_noncausal_fm.argtypes = [vp] * 4 + [i, vp] + [i] * 8 + [vp, sz, vp]
+    lib.la_fwd_noncausal_fm.restype = i
+    lib.la_bwd_causal_fm.argtypes = [vp] * 7 + [i, vp] + [i] * 8 + [vp, sz, vp]
+    lib.la_bwd_causal_fm.restype = i
+    lib.la_decode_step_fm.argtypes = [vp] * 6 + [i, vp] + [i] * 6 + [vp]
+    lib.la_decode_step_fm.restype = i
     if path is None:
         _lib = lib
     return lib

@@ -285,3 +285,122 @@ def la_decode_step_decay(S, z, q, k, v, gamma, o=None, stream=None):
                                           B, H, dk, dvv, _code(q), _stream(dev, stream))
     _lib.check(rc, "la_decode_step_decay")
     return o
+
+
+# ---------------------------------------------------------------------------
+# Feature maps: "elu1" (the default of every entry point above), "identity"
+# (q and k are the features) and "prf" (positive random features with the
+# directions W [H, m, d_k] in the dtype of q).
+# ---------------------------------------------------------------------------
+_FM = {"elu1": _lib.LA_PHI_ELU1, "identity": _lib.LA_PHI_IDENTITY, "prf": _lib.LA_PHI_PRF}
+
+
+def _fm_args(feature_map, W, q):
+    try:
+        code = _FM[feature_map]
+    except KeyError:
+        raise ValueError(f"feature_map must be one of {sorted(_FM)}") from None
+    if code != _lib.LA_PHI_PRF:
+        return code, None, q.shape[-1]
+    if W is None or W.dim() != 3 or W.dtype != q.dtype or W.shape[2] != q.shape[-1]:
+        raise ValueError("feature_map='prf' needs W [H, m, d_k] in the dtype of q")
+    _dev(W)
+    return code, W, W.shape[1]
+
+
+def la_fwd_causal_fm_workspace_bytes(B, H, N, d_k, d_v, C, feature_map, m, dtype) -> int:
+    return int(_lib.load().la_fwd_causal_fm_workspace_bytes(B, H, N, d_k, d_v, C, _FM[feature_map], m,
+                                                            _DT[dtype]))
+
+
+def la_fwd_noncausal_fm_workspace_bytes(B, H, N, d_k, d_v, feature_map, m, dtype) -> int:
+    return int(_lib.load().la_fwd_noncausal_fm_workspace_bytes(B, H, N, d_k, d_v, _FM[feature_map], m, _DT[dtype]))
+
+
+def la_bwd_causal_fm_workspace_bytes(B, H, N, d_k, d_v, C, feature_map, m, dtype) -> int:
+    return int(_lib.load().la_bwd_causal_fm_workspace_bytes(B, H, N, d_k, d_v, C, _FM[feature_map], m,
+                                                            _DT[dtype]))
+
+
+def la_fwd_causal_fm(q, k, v, feature_map="elu1", W=None, o=None, den=None, C: int = 64, out_dtype=None, ws=None,
+                     stream=None, want_den: bool = True):
+    """Causal forward with a feature map.  Returns (o, den)."""
+    B, H, N, dk, dv = _shapes(q, k, v)
+    dev = _dev(q, k, v, o, den, ws)
+    code, W, m = _fm_args(feature_map, W, q)
+    if o is None:
+        o = torch.empty((B, H, N, dv), dtype=out_dtype or q.dtype, device=dev)
+    if den is None and want_den:
+        den = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if tuple(o.shape) != (B, H, N, dv) or (den is not None and tuple(den.shape) != (B, H, N)):
+        raise ValueError("o must be [B,H,N,d_v] and den [B,H,N]")
+    _dev(o, den)
+    wp, wb = _ws(la_fwd_causal_fm_workspace_bytes(B, H, N, dk, dv, C, feature_map, m, q.dtype), dev, ws)
+    rc = _lib.load().la_fwd_causal_fm(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), code, _ptr(W), m,
+                                      B, H, N, dk, dv, C, _code(q), _code(o), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_fwd_causal_fm")
+    return o, den
+
+
+def la_fwd_noncausal_fm(q, k, v, feature_map="elu1", W=None, o=None, out_dtype=None, ws=None, stream=None):
+    """Non-causal forward with a feature map.  Returns o."""
+    B, H, N, dk, dv = _shapes(q, k, v)
+    dev = _dev(q, k, v, o, ws)
+    code, W, m = _fm_args(feature_map, W, q)
+    if o is None:
+        o = torch.empty((B, H, N, dv), dtype=out_dtype or q.dtype, device=dev)
+    if tuple(o.shape) != (B, H, N, dv):
+        raise ValueError("o must be [B,H,N,d_v]")
+    _dev(o)
+    wp, wb = _ws(la_fwd_noncausal_fm_workspace_bytes(B, H, N, dk, dv, feature_map, m, q.dtype), dev, ws)
+    rc = _lib.load().la_fwd_noncausal_fm(_ptr(q), _ptr(k), _ptr(v), _ptr(o), code, _ptr(W), m, B, H, N, dk, dv,
+                                         _code(q), _code(o), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_fwd_noncausal_fm")
+    return o
+
+
+def la_bwd_causal_fm(q, k, v, dO, feature_map="elu1", W=None, dq=None, dk=None, dv=None, C: int = 64, ws=None,
+                     stream=None):
+    """Backward of la_fwd_causal_fm.  Returns (dq, dk, dv) in the dtype of q."""
+    B, H, N, d_k, d_v = _shapes(q, k, v)
+    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
+    code, W, m = _fm_args(feature_map, W, q)
+    if tuple(dO.shape) != (B, H, N, d_v) or dO.dtype != q.dtype:
+        raise ValueError("dO must be [B,H,N,d_v] in the dtype of q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("dq, dk, dv must match q, k, v in shape and dtype")
+    _dev(dq, dk, dv)
+    wp, wb = _ws(la_bwd_causal_fm_workspace_bytes(B, H, N, d_k, d_v, C, feature_map, m, q.dtype), dev, ws)
+    rc = _lib.load().la_bwd_causal_fm(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), code,
+                                      _ptr(W), m, B, H, N, d_k, d_v, C, _code(q), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_bwd_causal_fm")
+    return dq, dk, dv
+
+
+def la_decode_step_fm(S, z, q, k, v, feature_map="elu1", W=None, o=None, stream=None):
+    """One decode step with a feature map, updating S [B,H,m',d_v] and z [B,H,m'] in
+    place (m' = m for random features, d_k otherwise).  Returns o [B,H,d_v]."""
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B,H,d_k] and v [B,H,d_v]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    B, H, dk = q.shape
+    dvv = v.shape[2]
+    code, W, m = _fm_args(feature_map, W, q)
+    mf = m if code == _lib.LA_PHI_PRF else dk
+    if tuple(S.shape) != (B, H, mf, dvv) or tuple(z.shape) != (B, H, mf) or S.dtype != torch.float32 \
+            or z.dtype != torch.float32:
+        raise ValueError(f"S must be float32 [B,H,{mf},d_v] and z float32 [B,H,{mf}]")
+    dev = _dev(S, z, q, k, v, o)
+    if o is None:
+        o = torch.empty((B, H, dvv), dtype=q.dtype, device=dev)
+    if tuple(o.shape) != (B, H, dvv) or o.dtype != q.dtype:
+        raise ValueError("o must be [B,H,d_v] in the dtype of q")
+    rc = _lib.load().la_decode_step_fm(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), code, _ptr(W), m,
+                                       B, H, dk, dvv, _code(q), _stream(dev, stream))
+    _lib.check(rc, "la_decode_step_fm")
+    return o

@@ -24,6 +24,7 @@ SOURCES = [
     "la_bwd.hip",
     "la_scan.hip",
     "la_noalloc.hip",
+    "la_prf.hip",
     "la_fwd_dk16.hip",
     "la_fwd_dk32.hip",
     "la_fwd_dk64.hip",

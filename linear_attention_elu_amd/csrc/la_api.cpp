@@ -112,8 +112,7 @@ using la::from_hip;
 using la::fwd_ws_bytes;
 using la::run_fwd;
 
-// Chunk size the non-causal path tiles its sequence with (not part of its ABI).
-constexpr int kNonCausalChunk = 64;
+using la::kNonCausalChunk;
 
 }  // namespace
 

@@ -75,6 +75,7 @@ struct BwdParams {
     int state_P;             // segments per bh in the state array
     int state_mult;          // fine segments per segment of this launch
     int sum_P;               // non-causal: the totals are the sums of slots 0 .. sum_P - 1
+    int phi_id;              // feature map: 0 = elu + 1, 1 = identity (phi' = 1)
 };
 
 template <typename TI, int DK, int DV> constexpr int bwd_cmax() {
@@ -118,8 +119,10 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
         }
     }
 
-    // phi of the loaded values, in place (16-byte vectors of TI).
-    __device__ __forceinline__ void apply_phi() {
+    // phi of the loaded values, in place (16-byte vectors of TI); nothing for
+    // the identity map.
+    __device__ __forceinline__ void apply_phi(bool ident) {
+        if (ident) return;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             float x[VEC];
@@ -203,6 +206,7 @@ la_bwd_dq_kernel(const BwdParams p) {
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + C - 1) / C;
     const int nib = C / 16;
+    const bool ident = p.phi_id != 0;  // uniform: identity feature map
     const bool active = EB >= NW || wave < EB;
     const int eb = wave;
 
@@ -258,8 +262,8 @@ la_bwd_dq_kernel(const BwdParams p) {
     };
     if (nch > 0) {
         fetch(0);
-        if constexpr (!NC) xk.apply_phi();
-        xq.apply_phi();
+        if constexpr (!NC) xk.apply_phi(ident);
+        xq.apply_phi(ident);
     }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
@@ -393,14 +397,14 @@ la_bwd_dq_kernel(const BwdParams p) {
                     f32x4 out;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        out[r] = (X[I][r] - Z[I][r] * coef) * inv * fminf(fq[r], 1.0f);
+                        out[r] = (X[I][r] - Z[I][r] * coef) * inv * (ident ? 1.0f : fminf(fq[r], 1.0f));
                     if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
                 }
             }
         }
         // phi of the next chunk's rows (after the last chunk the registers are not used again)
-        if constexpr (!NC) xk.apply_phi();
-        xq.apply_phi();
+        if constexpr (!NC) xk.apply_phi(ident);
+        xq.apply_phi(ident);
         if (active && !NC) {
             // state carry: S^T(c', eb) += V^T(c') phi(K)(eb), z(eb) += phi(K)(eb)^T 1
             // (token rows past the chunk are zero in the tiles)
@@ -466,6 +470,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     const int row_end = min(N, row_begin + p.L);
     const int nch = (row_end - row_begin + C - 1) / C;
     const int nib = C / 16;
+    const bool ident = p.phi_id != 0;  // uniform: identity feature map
     const bool has_e = EB >= NW || wave < EB, has_c = CB >= NW || wave < CB;
     const int eb = wave, cb = wave;
 
@@ -529,8 +534,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     };
     if (nch > 0) {
         fetch(nch - 1);
-        if constexpr (!NC) xq.apply_phi();
-        xk.apply_phi();
+        if constexpr (!NC) xq.apply_phi(ident);
+        xk.apply_phi(ident);
     }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
@@ -656,7 +661,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     const f32x4 kd = lds_get4(kb, 16 * J * SM::LK + 16 * eb);
                     f32x4 out;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out[r] = (acc[r] + accr[r]) * fminf(kd[r], 1.0f);
+                    for (int r = 0; r < 4; ++r) out[r] = (acc[r] + accr[r]) * (ident ? 1.0f : fminf(kd[r], 1.0f));
                     if (valid) store4<TI>(p.dk, orow * DK + 16 * eb + 4 * g, out);
                 }
                 if (has_c) {
@@ -681,8 +686,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             }
         }
         // phi of the previous chunk's rows (after the first chunk the registers are not used again)
-        if constexpr (!NC) xq.apply_phi();
-        xk.apply_phi();
+        if constexpr (!NC) xq.apply_phi(ident);
+        xk.apply_phi(ident);
         if (has_e && !NC) {
             // state carry: R^T(c', eb) += dO^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
             // (a = 0 for token rows past the chunk)

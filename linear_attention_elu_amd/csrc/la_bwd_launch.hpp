@@ -64,6 +64,7 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
 
     FwdParams a{};
     a.N = d.N;
+    a.phi_id = d.phi_id;
     a.L = Lf;
     a.state_P = Pf;
     a.state_mult = 1;
@@ -84,6 +85,7 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     b.dk = d.dk;
     b.dv = d.dv;
     b.N = d.N;
+    b.phi_id = d.phi_id;
     b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
     b.state_P = Pf;
     b.state_mult = 0;  // every segment reads slots 0 .. Pf - 1
@@ -176,6 +178,7 @@ hipError_t run_bwd_t(const BwdDesc &d) {
 
     FwdParams a{};
     a.N = d.N;
+    a.phi_id = d.phi_id;
     a.L = Lf;
     a.state_P = Pf;
     a.state_mult = 1;
@@ -203,6 +206,7 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     b.dk = d.dk;
     b.dv = d.dv;
     b.N = d.N;
+    b.phi_id = d.phi_id;
     b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
     b.state_P = Pf;
 

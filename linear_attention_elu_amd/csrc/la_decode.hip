@@ -15,20 +15,30 @@
 //
 // With a per-head decay (itwiki "선형 어텐션", table of later variants, RetNet
 // row) the update is S = gamma_h S + phi(k) v^T, z = gamma_h z + phi(k); a
-// null gamma is gamma = 1, the plain step.
+// null gamma is gamma = 1, the plain step.  The feature map is a template
+// parameter (elu + 1, identity, or positive random features computed per
+// step from the directions W).
 #include "la_device.hpp"
 #include "la_internal.h"
 
 namespace la {
 
-template <int DK, int DV, typename TI>
+// Feature maps of the decode step: FM_ELU1 phi = elu + 1 (DK = d_k), FM_ID
+// phi(x) = x (q and k are features), FM_PRF positive random features
+// phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(DK), r < DK, from the din-wide
+// q and k rows and the directions W [H][DK][din] (itwiki "선형 어텐션",
+// section "특징 사상 선택").
+enum { FM_ELU1 = 0, FM_ID = 1, FM_PRF = 2 };
+
+template <int DK, int DV, typename TI, int FM>
 __global__ void __launch_bounds__(256)
 la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__restrict__ q,
                  const void *__restrict__ k, const void *__restrict__ v, void *__restrict__ o, long BH,
-                 const float *__restrict__ gamma, int H) {
+                 const float *__restrict__ gamma, int H, const void *__restrict__ W, int din) {
     constexpr int CV = DV / 4;   // lanes per row of S (one float4 each)
     constexpr int RG = 64 / CV;  // rows of S a wave covers per access
     constexpr int RPL = DK / RG; // accesses per lane
+    constexpr int NFH = (DK + 63) / 64;  // features per lane (random features)
     const int lane = threadIdx.x & 63;
     const long bh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (bh >= BH) return;  // whole waves leave; no block-wide barrier follows
@@ -37,7 +47,50 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
     const int cg = lane % CV;
     const int r0 = lane / CV;
     float *Sb = S + bh * (long)DK * DV;
-    const long qk0 = bh * (long)DK;
+    const long qk0 = bh * (long)(FM == FM_PRF ? din : DK);
+
+    // Random features: lane l computes features l, l + 64 of q and k.
+    float fqh[NFH], fkh[NFH];
+    if constexpr (FM == FM_PRF) {
+        float nq = 0.f, nk = 0.f;
+        for (int i = 0; i < din; ++i) {
+            const float xq = Store<TI>::load(q, qk0 + i), xk = Store<TI>::load(k, qk0 + i);
+            nq += xq * xq;
+            nk += xk * xk;
+        }
+        const float scale = __builtin_amdgcn_rsqf((float)DK);
+#pragma unroll
+        for (int h = 0; h < NFH; ++h) {
+            const int e = lane + 64 * h;
+            float aq = 0.f, ak = 0.f;
+            if (e < DK) {
+                const long w0 = ((bh % H) * (long)DK + e) * din;
+                for (int i = 0; i < din; ++i) {
+                    const float w = Store<TI>::load(W, w0 + i);
+                    aq += w * Store<TI>::load(q, qk0 + i);
+                    ak += w * Store<TI>::load(k, qk0 + i);
+                }
+            }
+            fqh[h] = __expf(aq - 0.5f * nq) * scale;
+            fkh[h] = __expf(ak - 0.5f * nk) * scale;
+        }
+    }
+    // phi(q_e), phi(k_e) for a feature index e (wave-uniform control flow)
+    auto feat = [&](const void *x, const float (&fh)[NFH], int e) {
+        if constexpr (FM == FM_PRF) {
+            float r = __shfl(fh[0], e & 63, 64);
+#pragma unroll
+            for (int h = 1; h < NFH; ++h) {
+                const float t = __shfl(fh[h], e & 63, 64);
+                r = (e >> 6) == h ? t : r;
+            }
+            return r;
+        } else if constexpr (FM == FM_ID) {
+            return Store<TI>::load(x, qk0 + e);
+        } else {
+            return phi(Store<TI>::load(x, qk0 + e));
+        }
+    };
 
     float vv[4];
 #pragma unroll
@@ -56,8 +109,8 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
 #pragma unroll
         for (int t = 0; t < GRP; ++t) {
             const int e = r0 + RG * (t0 + t);
-            const float fk = phi(Store<TI>::load(k, qk0 + e));
-            const float fq = phi(Store<TI>::load(q, qk0 + e));
+            const float fk = feat(k, fkh, e);
+            const float fq = feat(q, fqh, e);
             f32x4 s = sreg[t];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -78,9 +131,20 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
     for (int h = 0; h < (DK + 63) / 64; ++h) {
         const int e = lane + 64 * h;
         if (e < DK) {
-            const float zn = gm * z[qk0 + e] + phi(Store<TI>::load(k, qk0 + e));
-            z[qk0 + e] = zn;
-            dpart += phi(Store<TI>::load(q, qk0 + e)) * zn;
+            float fk, fq;
+            if constexpr (FM == FM_PRF) {
+                fk = fkh[h];
+                fq = fqh[h];
+            } else if constexpr (FM == FM_ID) {
+                fk = Store<TI>::load(k, qk0 + e);
+                fq = Store<TI>::load(q, qk0 + e);
+            } else {
+                fk = phi(Store<TI>::load(k, qk0 + e));
+                fq = phi(Store<TI>::load(q, qk0 + e));
+            }
+            const float zn = gm * z[bh * (long)DK + e] + fk;
+            z[bh * (long)DK + e] = zn;
+            dpart += fq * zn;
         }
     }
 #pragma unroll
@@ -100,14 +164,29 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
     }
 }
 
+template <int DK, int DV, typename TI>
+static void launch_decode(const DecodeDesc &d, dim3 grid, long BH) {
+    switch (d.fm) {
+        case FM_ID:
+            la_decode_kernel<DK, DV, TI, FM_ID><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH, d.gamma,
+                                                                            d.H, nullptr, d.DK);
+            break;
+        case FM_PRF:
+            la_decode_kernel<DK, DV, TI, FM_PRF><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH,
+                                                                             d.gamma, d.H, d.W, d.din);
+            break;
+        default:
+            la_decode_kernel<DK, DV, TI, FM_ELU1><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH,
+                                                                              d.gamma, d.H, nullptr, d.DK);
+    }
+}
+
 template <int DK, int DV>
 static hipError_t run_decode_t(const DecodeDesc &d) {
     const long BH = (long)d.B * d.H;
     const dim3 grid((unsigned)((BH + 3) / 4));
-    if (d.in_bf16)
-        la_decode_kernel<DK, DV, __bf16><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH, d.gamma, d.H);
-    else
-        la_decode_kernel<DK, DV, float><<<grid, 256, 0, d.stream>>>(d.S, d.z, d.q, d.k, d.v, d.o, BH, d.gamma, d.H);
+    if (d.in_bf16) launch_decode<DK, DV, __bf16>(d, grid, BH);
+    else launch_decode<DK, DV, float>(d, grid, BH);
     return hipGetLastError();
 }
 

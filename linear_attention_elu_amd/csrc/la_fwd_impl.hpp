@@ -89,6 +89,7 @@ struct FwdParams {
     const float *gamma;     // MODE_CAUSAL, MODE_AGG: per-head decay [H], or null for none
     int H;                  // heads (bh % H is the head of workgroup column bh)
     int sum_P;              // MODE_APPLY: the total state is the sum of slots 0 .. sum_P - 1 (>= 1)
+    int phi_id;             // feature map: 0 = elu + 1, 1 = identity (q and k are already features)
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -318,12 +319,16 @@ la_chunk_kernel(const FwdParams p) {
                 kdec[i] = powi(gam, DM - rq0 - i * RSQ);
             }
         }
+        const bool ident = p.phi_id != 0;  // uniform: the feature map is the identity
         auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
             float x[VEC];
             unpack16(u, x, TI());
             Frag<TC> w;
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) w.set(t, (WEIGHTED || decay) ? phi(x[t]) * scale : phi(x[t]));
+            for (int t = 0; t < VEC; ++t) {
+                const float f = ident ? x[t] : phi(x[t]);
+                w.set(t, (WEIGHTED || decay) ? f * scale : f);
+            }
             if constexpr (sizeof(TC) == 2) {
                 return __builtin_bit_cast(uint4, w.v);
             } else {

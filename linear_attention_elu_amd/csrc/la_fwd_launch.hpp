@@ -58,6 +58,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.den = d.den;
     p.N = d.N;
     p.state_P = Pf;
+    p.phi_id = d.phi_id;
     hipError_t err;
 
     if (causal) {

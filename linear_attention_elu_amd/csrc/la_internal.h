@@ -23,6 +23,7 @@ struct FwdDesc {
     hipStream_t stream;
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
     long ws_states;      // causal only: if > 0, at most this many segment states fit the workspace
+    int phi_id;          // feature map: 0 = elu + 1, 1 = identity (q, k are already features)
 };
 
 struct DecodeDesc {
@@ -33,6 +34,9 @@ struct DecodeDesc {
     int in_bf16;
     hipStream_t stream;
     const float *gamma;  // per-head decay [H] (device), or null for none
+    int fm;              // feature map: 0 = elu + 1, 1 = identity, 2 = random features (DK = their count)
+    const void *W;       // random features: directions [H][DK][din] in the input type
+    int din;             // random features: width of q and k
 };
 
 struct BwdDesc {
@@ -44,6 +48,7 @@ struct BwdDesc {
     float *ws;
     hipStream_t stream;
     int noncausal;  // gradient of the non-causal form (full sums)
+    int phi_id;     // feature map: 0 = elu + 1, 1 = identity
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a
@@ -78,6 +83,30 @@ inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
                            int mode, int lim, hipStream_t stream, const float *gamma = nullptr, int H = 1,
                            int L = 0);
+
+// Shared argument predicates and sizes of the entry points (la_api.cpp).
+bool dim_ok(int d);
+bool chunk_ok(int C);
+bool dtype_ok(int t);
+bool aligned(const void *p);
+bool aligned_or_null(const void *p);
+la_status check_shape(int B, int H, int N);
+la_status from_hip(hipError_t e);
+size_t fwd_ws_bytes(int B, int H, int N, int dk, int dv, int C, bool causal);
+// Chunk size the non-causal path tiles its sequence with (not part of its ABI).
+constexpr int kNonCausalChunk = 64;
+
+// The random-feature map and its backward (la_prf.hip), x [BH][N][DK] and the
+// directions W [H][M][DK] in the input type:
+//   PRF_PHI      out = phi(x) [BH][N][M] in the input type;
+//   PRF_PHI_F32  out = phi(x) in fp32;
+//   PRF_VJP      out = dx [BH][N][DK] (input type) from x, f = phi(x) and
+//                df = dphi, both fp32.
+enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2 };
+hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const void *f, const void *df, void *out,
+                      long BH, int N, int H, int DK, int M, hipStream_t stream);
+// n values bf16 -> fp32 (to_f32) or fp32 -> bf16 (round to nearest even).
+hipError_t launch_convert(bool to_f32, const void *a, void *b, long n, hipStream_t stream);
 
 // Argument checks of the causal forward entry points (all but the workspace),
 // before any HIP call; the status the entry point returns.

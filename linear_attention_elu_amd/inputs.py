@@ -48,3 +48,26 @@ def to_torch(x: np.ndarray, dtype, device):
     import torch
 
     return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(dtype).contiguous()
+
+
+def random_features(H: int, m: int, dk: int, seed: int = 0, orthogonal: bool = True) -> np.ndarray:
+    """m random directions of dimension dk per head, [H, m, dk] float32, drawn from
+    N(0, I); with `orthogonal`, in blocks of dk mutually orthogonal directions
+    (the Q factor of a Gaussian matrix) whose lengths are drawn independently
+    like those of N(0, I) vectors, so each direction is still N(0, I) in
+    distribution.  Input generation only: the directions are a random input of
+    the random-feature map."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((H, m, dk), np.float64)
+    for h in range(H):
+        if not orthogonal:
+            out[h] = rng.standard_normal((m, dk))
+            continue
+        rows = []
+        while sum(r.shape[0] for r in rows) < m:
+            qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+            rows.append(qm.T)
+        blk = np.concatenate(rows, 0)[:m]
+        lengths = np.linalg.norm(rng.standard_normal((m, dk)), axis=1)
+        out[h] = blk * lengths[:, None]
+    return out.astype(np.float32)

@@ -204,6 +204,36 @@ def test_fwd_causal_noalloc_rejects(lib):
     assert f(*bad) == 7
 
 
+def test_feature_map_entry_points_reject(lib):
+    f = lib.la_fwd_causal_fm
+    args = [P] * 4 + [None] + [2, P, 64] + [1, 1, 64, 64, 64, 64, 1, 1, P, 1 << 24, None]
+    assert f(*args[:5], 7, *args[6:]) == 3           # unknown feature map
+    bad = list(args)
+    bad[6] = None                                     # random features without W
+    assert f(*bad) == 1
+    bad = list(args)
+    bad[7] = 48                                       # m
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[11] = 16                                      # d_k = 16 with random features
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[6] = MIS                                      # W alignment
+    assert f(*bad) == 7
+    bad = list(args)
+    bad[-3] = None                                    # workspace (the features need one)
+    bad[-2] = 0
+    assert f(*bad) == 5
+    assert la.la_fwd_causal_fm_workspace_bytes(1, 1, 64, 64, 64, 64, "prf", 64, __import__("torch").bfloat16) > 0
+    assert lib.la_fwd_causal_fm_workspace_bytes(1, 1, 64, 64, 64, 64, 9, 64, 1) == 0
+    g = lib.la_decode_step_fm
+    assert g(P, P, P, P, P, P, 2, None, 64, 1, 1, 64, 64, 1, None) == 1
+    assert g(P, P, P, P, P, P, 2, P, 16, 1, 1, 64, 64, 1, None) == 3
+    h = lib.la_bwd_causal_fm
+    assert h(*([P] * 7), 5, None, 64, 1, 1, 64, 64, 64, 64, 1, P, 1 << 24, None) == 3
+    assert h(*([P] * 7), 2, P, 64, 1, 1, 64, 64, 64, 64, 1, P, 16, None) == 5
+
+
 def test_decode_decay_rejects(lib):
     f = lib.la_decode_step_decay
     assert f(P, P, P, P, P, P, None, 1, 1, 32, 32, 0, None) == 1
