@@ -17,7 +17,8 @@ resident in HBM.  Alongside it, on the same JSON line:
   extra         the length sweep N = 2^9 .. 2^16 (forward and backward time,
                 peak device bytes per call), the non-causal workload
                 (B=4, H=8, N=4096, d=64), the forward and backward at
-                B=8, H=16, N=8192, d=128, C=64, and the decay forward;
+                B=8, H=16, N=8192, d=128, C=64, the decay forward and the
+                forward with random features (m = 64) at the headline shape;
   cpu_baseline  the fp64 CPU oracle timed on the host cores on a bounded sample
                 of the headline workload.
 Inputs are seeded synthetic normals.  One GPU only.
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="skip the sweep / non-causal / backward lines")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "decay", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "decay", "prf", "copy"], default=None,
                     help="run one leg only (for profiler runs); prints its own JSON line")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the plain copy leg")
     return ap.parse_args()
@@ -186,6 +187,33 @@ def bench_fwd_decay(steps, warmup, dev, B=8, H=8, N=65536, d=64, C=64, seed=0):
                     torch.cuda.current_stream(dev))
     by = B * H * N * 4 * d * 2
     return {"workload": f"causal_decay_fwd_bf16_B{B}_H{H}_N{N}_d{d}_C{C}", "us": round(ms * 1e3, 2),
+            "tokens_per_s": round(B * N / (ms * 1e-3), 1), "achieved_GBs": round(by / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def bench_fwd_prf(steps, warmup, dev, B=8, H=8, N=65536, d=64, m=64, C=64, seed=0):
+    """The headline shape with Performer's positive random features (m = 64
+    directions per head, orthogonal blocks): q, k ~ N(0, d^-1/2), as the map is
+    used.  Algorithmic bytes are the call's inputs and output (q, k, v read, o
+    written: 512 B per token-head; W is 8 KB per head); the features pass through
+    the workspace (2 x m x 2 B written and read per token-head), which the
+    fraction does not count as useful bytes."""
+    import torch
+
+    import linear_attention_elu_amd as la
+    from linear_attention_elu_amd import inputs
+
+    host = inputs.attention_inputs(B, H, N, d, d, seed=seed, qk_std=d ** -0.25)
+    q, k, v = (inputs.to_torch(host[n], torch.bfloat16, dev) for n in ("q", "k", "v"))
+    del host
+    W = inputs.to_torch(inputs.random_features(H, m, d, seed=seed + 1), torch.bfloat16, dev)
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, la.la_fwd_causal_fm_workspace_bytes(B, H, N, d, d, C, "prf", m, torch.bfloat16)),
+                     dtype=torch.uint8, device=dev)
+    ms = time_calls(lambda: la.la_fwd_causal_fm(q, k, v, "prf", W, o=o, C=C, ws=ws, want_den=False), steps, warmup,
+                    torch.cuda.current_stream(dev))
+    by = B * H * N * 4 * d * 2
+    return {"workload": f"causal_prf_fwd_bf16_B{B}_H{H}_N{N}_d{d}_m{m}_C{C}", "us": round(ms * 1e3, 2),
             "tokens_per_s": round(B * N / (ms * 1e-3), 1), "achieved_GBs": round(by / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -402,6 +430,8 @@ def main():
             r = bench_bwd(dev, args.steps, args.warmup)
         elif args.only == "decay":
             r = bench_fwd_decay(args.steps, args.warmup, dev)
+        elif args.only == "prf":
+            r = bench_fwd_prf(args.steps, args.warmup, dev)
         else:
             r = bench_copy(dev, args.copy_mib, args.steps, args.warmup)
         print(json.dumps({"only": args.only, **r}))
@@ -451,7 +481,8 @@ def main():
         for e in range(9, 17):
             sweep[str(2 ** e)] = bench_sweep_point(dev, 2 ** e, max(5, args.steps), 20)
         res["extra"] = {"causal_sweep_B8_H8_d64_C64": sweep, "noncausal": bench_noncausal(dev),
-                        "fwd_bwd": bench_bwd(dev), "causal_decay": bench_fwd_decay(args.steps, args.warmup, dev)}
+                        "fwd_bwd": bench_bwd(dev), "causal_decay": bench_fwd_decay(args.steps, args.warmup, dev),
+                        "causal_prf": bench_fwd_prf(args.steps, args.warmup, dev)}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on host cores")
         res["cpu_baseline"] = cpu_baseline()
