@@ -161,9 +161,9 @@ la_status la_fwd_causal_state(const void *q, const void *k, const void *v, void 
  *   S_i = gamma_h S_{i-1} + phi(k_i) v_i^T,  z_i = gamma_h z_{i-1} + phi(k_i),
  *   o_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
  * gamma: device pointer to H fp32 values, gamma_h for head h, each in
- * [0.25, 1] (the chunked evaluation folds gamma^(+-(C/2 + 1)) into its
- * operands; smaller values leave the fp32 range).  A NULL gamma is no decay
- * (la_fwd_causal_state).  S0, z0 enter decayed like any earlier state; S_out,
+ * [0, 1] (gamma = 0 keeps only the current token: out_i = v_i).  The chunked
+ * evaluation applies only powers gamma^e with e >= 0, so every value in the
+ * range is exact to rounding.  A NULL gamma is no decay (la_fwd_causal_state).  S0, z0 enter decayed like any earlier state; S_out,
  * z_out receive the decayed state after the last token and seed
  * la_decode_step_decay.  Other arguments, the workspace (the query of
  * la_fwd_causal) and errors as la_fwd_causal_state.
@@ -214,6 +214,24 @@ la_status la_bwd_causal(const void *q, const void *k, const void *v, const void 
                         void *dq, void *dk, void *dv,
                         int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of la_fwd_causal_decay (itwiki "선형 어텐션", table of later
+ * variants, RetNet row; the gradient as cumulative sums with linear memory,
+ * velog 3.5): the exact gradient with respect to q, k and v of the decayed
+ * causal form with zero initial state.  It is the gradient of la_bwd_causal
+ * with every pair (i, j <= i) weighed by gamma_h^(i - j):
+ *   dphi(q_i) = S_i gh_i + eps_i z_i        (decayed prefix sums S_i, z_i)
+ *   dphi(k_j) = R_j v_j + r_j,  dv_j = R_j^T phi(k_j),
+ *   R_j = sum_{i>=j} gamma^(i - j) phi(q_i) gh_i^T,  r_j likewise with eps_i.
+ * gamma: device pointer to H fp32 values in [0, 1] (NULL returns
+ * LA_ERR_NULL_PTR).  Other arguments, the workspace (the query of
+ * la_bwd_causal) and errors as la_bwd_causal.
+ */
+la_status la_bwd_causal_decay(const void *q, const void *k, const void *v, const void *dO,
+                              void *dq, void *dk, void *dv, const float *gamma,
+                              int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
+                              void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward of the non-causal form (blog digest "Method / key components 2)";

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     la_fwd_noncausal,
     la_bwd_causal,
     la_bwd_noncausal,
+    la_bwd_causal_decay,
     la_decode_step,
     la_decode_step_decay,
     la_fwd_causal_fm_workspace_bytes,

@@ -35,6 +35,7 @@ EXPORTS = (
     "la_fwd_causal_noalloc",
     "la_bwd_causal",
     "la_bwd_noncausal",
+    "la_bwd_causal_decay",
     "la_decode_step",
     "la_decode_step_decay",
     "la_fwd_causal_fm_workspace_bytes",
@@ -89,6 +90,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.la_fwd_causal_state.restype = i
     lib.la_bwd_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.la_bwd_causal.restype = i
+    lib.la_bwd_causal_decay.argtypes = [vp] * 8 + [i] * 7 + [vp, sz, vp]
+    lib.la_bwd_causal_decay.restype = i
     lib.la_bwd_noncausal_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.la_bwd_noncausal_workspace_bytes.restype = sz
     lib.la_bwd_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]

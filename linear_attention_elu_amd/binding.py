@@ -116,7 +116,7 @@ def la_fwd_causal_state(q, k, v, o=None, den=None, S0=None, z0=None, S_out=None,
 def la_fwd_causal_decay(q, k, v, gamma, o=None, den=None, S0=None, z0=None, S_out=None, z_out=None,
                         C: int = 64, out_dtype=None, ws=None, stream=None, want_den: bool = True):
     """Causal forward with a fixed decay gamma[h] per head (float32 [H] on the
-    device, values in [0.25, 1]) and an optional carried state.  Returns (o, den)."""
+    device, values in [0, 1]) and an optional carried state.  Returns (o, den)."""
     B, H, N, dk, dv = _shapes(q, k, v)
     dev = _dev(q, k, v, o, den, S0, z0, S_out, z_out, ws)
     _gamma(gamma, H, dev)
@@ -210,6 +210,28 @@ def la_bwd_causal(q, k, v, dO, dq=None, dk=None, dv=None, C: int = 64, ws=None, 
     rc = _lib.load().la_bwd_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
                                    B, H, N, d_k, d_v, C, _code(q), wp, wb, _stream(dev, stream))
     _lib.check(rc, "la_bwd_causal")
+    return dq, dk, dv
+
+
+def la_bwd_causal_decay(q, k, v, dO, gamma, dq=None, dk=None, dv=None, C: int = 64, ws=None, stream=None):
+    """Backward of la_fwd_causal_decay (per-head decay gamma, float32 [H] on the
+    device).  Returns (dq, dk, dv) in the dtype of q."""
+    B, H, N, d_k, d_v = _shapes(q, k, v)
+    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
+    _gamma(gamma, H, dev)
+    if tuple(dO.shape) != (B, H, N, d_v) or dO.dtype != q.dtype:
+        raise ValueError("dO must be [B,H,N,d_v] in the dtype of q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError("dq, dk, dv must match q, k, v in shape and dtype")
+    _dev(dq, dk, dv)
+    wp, wb = _ws(la_bwd_causal_workspace_bytes(B, H, N, d_k, d_v, C), dev, ws)
+    rc = _lib.load().la_bwd_causal_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                                         _ptr(gamma), B, H, N, d_k, d_v, C, _code(q), wp, wb, _stream(dev, stream))
+    _lib.check(rc, "la_bwd_causal_decay")
     return dq, dk, dv
 
 

@@ -217,6 +217,27 @@ la_status la_bwd_causal(const void *q, const void *k, const void *v, const void 
     return from_hip(la::run_bwd(d));
 }
 
+la_status la_bwd_causal_decay(const void *q, const void *k, const void *v, const void *dO,
+                              void *dq, void *dk, void *dv, const float *gamma,
+                              int B, int H, int N, int d_k, int d_v, int C, la_dtype in,
+                              void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!gamma) return LA_ERR_NULL_PTR;
+    if ((reinterpret_cast<uintptr_t>(gamma) & 3u) != 0) return LA_ERR_ALIGNMENT;
+    if (!q || !k || !v || !dO || !dq || !dk || !dv) return LA_ERR_NULL_PTR;
+    la_status st = check_shape(B, H, N);
+    if (st != LA_OK) return st;
+    if (!dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return LA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in)) return LA_ERR_BAD_DTYPE;
+    if (!aligned(q) || !aligned(k) || !aligned(v) || !aligned(dO) || !aligned(dq) || !aligned(dk) ||
+        !aligned(dv) || !aligned_or_null(ws))
+        return LA_ERR_ALIGNMENT;
+    const size_t need = la::bwd_workspace_bytes(B, H, N, d_k, d_v, C);
+    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream,
+                  0, 0, gamma};
+    return from_hip(la::run_bwd(d));
+}
+
 la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const void *dO,
                            void *dq, void *dk, void *dv,
                            int B, int H, int N, int d_k, int d_v, la_dtype in,

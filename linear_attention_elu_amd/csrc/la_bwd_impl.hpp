@@ -76,6 +76,25 @@ struct BwdParams {
     int state_mult;          // fine segments per segment of this launch
     int sum_P;               // non-causal: the totals are the sums of slots 0 .. sum_P - 1
     int phi_id;              // feature map: 0 = elu + 1, 1 = identity (phi' = 1)
+    const float *gamma;      // DECAY: per-head decay [H]
+    int H;                   // heads (bh % H is the head of workgroup column bh)
+};
+
+// Per-head decay (itwiki "선형 어텐션", table of later variants, RetNet row):
+// S_i = gamma S_{i-1} + phi(k_i) v_i^T, z likewise.  Its gradient is the one
+// above with every pair (i, j <= i) weighed by gamma^(i - j): the in-chunk
+// products M and A carry gamma^(tau_i - tau_j) (tau the row in the chunk), the
+// dq sweep reads the carried S, z as gamma^(tau_i + 1) S, and the dk/dv sweep
+// reads the suffix state entering from the right, normalised at the next
+// chunk's first token, as gamma^(R - tau_j) R (R the rows of the chunk).  The
+// carries are S = gamma^R S + sum_j gamma^(R - 1 - tau_j) phi(k_j) v_j^T and
+// R = gamma^R R + sum_i gamma^(tau_i) (phi(q_i) a_i) g_i^T.  All exponents are
+// >= 0, so any gamma in [0, 1] is in range.
+struct Decay {
+    float lg;  // log2(gamma): -inf for gamma = 0
+    __device__ __forceinline__ float pow(int e) const {  // gamma^e, e >= 0
+        return e <= 0 ? 1.0f : __builtin_amdgcn_exp2f((float)e * lg);
+    }
 };
 
 template <typename TI, int DK, int DV> constexpr int bwd_cmax() {
@@ -167,7 +186,7 @@ __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
 // ---------------------------------------------------------------------------
 // dq sweep (forward over chunks, state S, z).
 // ---------------------------------------------------------------------------
-template <int DK, int DV, typename TI> struct DqSmem {
+template <int DK, int DV, typename TI, bool DEC = false> struct DqSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
     static constexpr int LK = BwdLd<TI, DK>::TR;   // phi(K): transpose reads
     static constexpr int LQ = BwdLd<TI, DK>::ROW;  // phi(Q): row reads
@@ -182,13 +201,17 @@ template <int DK, int DV, typename TI> struct DqSmem {
     alignas(16) TI mh[CM * LM];
     alignas(16) TI ml[LO ? CM * LM : 4];
     alignas(16) float red[kBwdWaves][CM][2];  // per-wave partial phi(q).X and phi(q).z
+    // decay weights gamma^(i - j) of query i and token j <= i, as value + remainder
+    alignas(16) TI dh[DEC ? CM * LM : 8];
+    alignas(16) TI dl[DEC && LO ? CM * LM : 8];
 };
 
-template <int DK, int DV, typename TI, bool NC = false>
+template <int DK, int DV, typename TI, bool NC = false, bool DECAY = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dq_kernel(const BwdParams p) {
     using TC = TI;
-    using SM = DqSmem<DK, DV, TI>;
+    constexpr bool dec = DECAY && !NC;
+    using SM = DqSmem<DK, DV, TI, dec>;
     constexpr int NW = kBwdWaves;
     constexpr int EB = DK / 16;          // feature blocks, one per wave
     constexpr int CV = DV / 16;          // value tiles of the state
@@ -214,6 +237,16 @@ la_bwd_dq_kernel(const BwdParams p) {
         uint32_t *w = reinterpret_cast<uint32_t *>(&sm);
         for (int i = tid; i < (int)(sizeof(SM) / 4); i += kBwdThreads) w[i] = 0u;
     }
+    const Decay dcy{dec ? __builtin_log2f(p.gamma[bh % p.H]) : 0.0f};
+    if constexpr (dec) {
+        __syncthreads();  // the zero fill is done; the first chunk's barrier orders these writes
+        for (int idx = tid; idx < SM::CM * SM::CM; idx += kBwdThreads) {
+            const int i = idx / SM::CM, j = idx % SM::CM;
+            const float w = j <= i ? dcy.pow(i - j) : 0.0f;
+            sm.dh[i * SM::LM + j] = static_cast<TC>(w);
+            if constexpr (SM::LO) sm.dl[i * SM::LM + j] = static_cast<TC>(w - static_cast<float>(static_cast<TC>(w)));
+        }
+    }
 
     // S^T(c', eb) tiles: lane (pp, g) holds S[16 eb + pp][16 c' + 4g + r]; z(eb): z[16 eb + 4g + r].
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -234,10 +267,11 @@ la_bwd_dq_kernel(const BwdParams p) {
         }
     }
     Frag<TC> fragS[NSV];  // S rows e, split over the value index
-    // Non-causal with bf16 operands: the total S also as its rounding
+    // Non-causal, or decayed, with bf16 operands: S also as its rounding
     // remainder, so that X = S g and z meet at fp32-level accuracy in
-    // X - z (phi(q) . X) / den, whose two terms cancel exactly for a single token.
-    constexpr bool SLO = NC && sizeof(TC) == 2;
+    // X - z (phi(q) . X) / den, whose two terms cancel exactly for a single
+    // token (non-causal) and to O(gamma) of their size for a fast decay.
+    constexpr bool SLO = (NC || dec) && sizeof(TC) == 2;
     Frag<TC> fragS_lo[SLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
@@ -272,6 +306,8 @@ la_bwd_dq_kernel(const BwdParams p) {
     const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 16 * eb + 4 * g);
     const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
     const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
+    const lds_vptr<TC> dhb = lds_v(sm.dh + (dec ? pp * SM::LM + 4 * g : 0));
+    const lds_vptr<TC> dlb = lds_v(sm.dl + (dec && SM::LO ? pp * SM::LM + 4 * g : 0));
 
     for (int ch = 0; ch < nch; ++ch) {
         const int r0 = row_begin + ch * C;
@@ -307,8 +343,11 @@ la_bwd_dq_kernel(const BwdParams p) {
             }
             // lane: tokens j = 16 J + 4g + r of query i = 16 I + pp
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (I == J && 4 * g + r > pp) acc[r] = 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int e = 16 * (I - J) + pp - 4 * g - r;  // i - j
+                if (I == J && e < 0) acc[r] = 0.f;
+                else if constexpr (dec) acc[r] *= dcy.pow(e);
+            }
             const int off = (16 * I + pp) * SM::LM + 16 * J + 4 * g;
             lds_put4_pair(sm.mh + off, sm.ml + (SM::LO ? off : 0), acc);
         }
@@ -331,6 +370,16 @@ la_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
                     for (int s = 0; s < NSV; ++s) lds_frag_split_v(fg[s], gb, 16 * I * SM::LG + 32 * s);
                     f32x4 ax = zero4, az = accZ;
+                    if constexpr (dec) {  // the carried state's terms first, decayed by gamma^(tau_i + 1)
+#pragma unroll
+                        for (int s = 0; s < NSV; ++s) {
+                            ax = mma(fragS[s], fg[s], ax);
+                            if constexpr (SLO) ax = mma(fragS_lo[s], fg[s], ax);
+                        }
+                        const float gi = dcy.pow(16 * I + pp + 1);
+                        ax = ax * gi;
+                        az = accZ * gi;
+                    }
 #pragma unroll
                     for (int jp = 0; jp < NTS; ++jp) {
                         if (!NC && 2 * jp <= I) {
@@ -341,19 +390,30 @@ la_bwd_dq_kernel(const BwdParams p) {
                                 lds_frag_split_v(fm, mlb, 16 * I * SM::LM + 32 * jp);
                                 ax = mma(fkt[jp], fm, ax);
                             }
-                            const int i = 16 * I + pp;
+                            if constexpr (dec) {  // decay weights over the same tokens (value + remainder)
+                                lds_frag_split_v(ftr, dhb, 16 * I * SM::LM + 32 * jp);
+                                az = mma(fkt[jp], ftr, az);
+                                if constexpr (SM::LO) {
+                                    lds_frag_split_v(ftr, dlb, 16 * I * SM::LM + 32 * jp);
+                                    az = mma(fkt[jp], ftr, az);
+                                }
+                            } else {
+                                const int i = 16 * I + pp;
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) {  // causal all-ones mask over the same tokens
-                                ftr.set(t, 32 * jp + 4 * g + t <= i ? 1.f : 0.f);
-                                ftr.set(t + 4, 32 * jp + 16 + 4 * g + t <= i ? 1.f : 0.f);
+                                for (int t = 0; t < 4; ++t) {  // causal all-ones mask over the same tokens
+                                    ftr.set(t, 32 * jp + 4 * g + t <= i ? 1.f : 0.f);
+                                    ftr.set(t + 4, 32 * jp + 16 + 4 * g + t <= i ? 1.f : 0.f);
+                                }
+                                az = mma(fkt[jp], ftr, az);
                             }
-                            az = mma(fkt[jp], ftr, az);
                         }
                     }
+                    if constexpr (!dec) {
 #pragma unroll
-                    for (int s = 0; s < NSV; ++s) {
-                        ax = mma(fragS[s], fg[s], ax);
-                        if constexpr (SLO) ax = mma(fragS_lo[s], fg[s], ax);
+                        for (int s = 0; s < NSV; ++s) {
+                            ax = mma(fragS[s], fg[s], ax);
+                            if constexpr (SLO) ax = mma(fragS_lo[s], fg[s], ax);
+                        }
                     }
                     const f32x4 fq = lds_get4(qb, 16 * I * SM::LQ);
                     float px = 0.f, pz = 0.f;
@@ -407,9 +467,23 @@ la_bwd_dq_kernel(const BwdParams p) {
         xq.apply_phi(ident);
         if (active && !NC) {
             // state carry: S^T(c', eb) += V^T(c') phi(K)(eb), z(eb) += phi(K)(eb)^T 1
-            // (token rows past the chunk are zero in the tiles)
+            // (token rows past the chunk are zero in the tiles; with decay the
+            // state first decays by gamma^R and token j weighs gamma^(R - 1 - tau_j))
+            if constexpr (dec) {
+                const float gR = dcy.pow(nrows);
+                accZ = accZ * gR;
+#pragma unroll
+                for (int cv = 0; cv < CV; ++cv) accS[cv] = accS[cv] * gR;
+            }
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
+                if constexpr (dec) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int tok = 32 * s + (t < 4 ? 4 * g + t : 16 + 4 * g + t - 4);
+                        fkt[s].set(t, tok < nrows ? fkt[s].get(t) * dcy.pow(nrows - 1 - tok) : 0.0f);
+                    }
+                }
                 accZ = mma(fkt[s], ones, accZ);
 #pragma unroll
                 for (int cv = 0; cv < CV; ++cv) {
@@ -448,10 +522,11 @@ template <int DK, int DV, typename TI> struct DkvSmem {
     alignas(16) float a[CM];  // a = 1 / den
 };
 
-template <int DK, int DV, typename TI, bool NC = false>
+template <int DK, int DV, typename TI, bool NC = false, bool DECAY = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dkdv_kernel(const BwdParams p) {
     using TC = TI;
+    constexpr bool dec = DECAY && !NC;
     using SM = DkvSmem<DK, DV, TI>;
     constexpr int NW = kBwdWaves;
     constexpr int EB = DK / 16, CB = DV / 16, CV = DV / 16;
@@ -479,6 +554,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         for (int i = tid; i < (int)(sizeof(SM) / 4); i += kBwdThreads) w[i] = 0u;
     }
     __syncthreads();
+    const Decay dcy{dec ? __builtin_log2f(p.gamma[bh % p.H]) : 0.0f};
 
     // R^T(c', eb) tiles: lane (pp, g) holds R[16 eb + pp][16 c' + 4g + r]; r(eb): r[16 eb + 4g + r].
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -501,9 +577,10 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         }
     }
     Frag<TC> fragR[NSV];  // R rows e, split over the value index
-    // Non-causal with bf16 operands: R also as its rounding remainder, so that
-    // R v_j and r meet at fp32-level accuracy (they cancel for a single token).
-    constexpr bool RLO = NC && sizeof(TC) == 2;
+    // Non-causal, or decayed, with bf16 operands: R also as its rounding
+    // remainder, so that R v_j and r meet at fp32-level accuracy (they cancel
+    // for a single token, and to O(gamma) of their size for a fast decay).
+    constexpr bool RLO = (NC || dec) && sizeof(TC) == 2;
     Frag<TC> fragR_lo[RLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
@@ -601,8 +678,10 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             const f32x4 av = *reinterpret_cast<const f32x4 *>(&sm.a[16 * I + 4 * g]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool keep = !(I == J && pp > 4 * g + r);
-                acc[r] = keep ? (is_a ? acc[r] : acc[r] + ev[r]) * av[r] : 0.f;
+                const int e = 16 * (I - J) + 4 * g + r - pp;  // i - j
+                const bool keep = !(I == J && e < 0);
+                const float w = dec && keep ? dcy.pow(e) : 1.0f;
+                acc[r] = keep ? (is_a ? acc[r] : acc[r] + ev[r]) * av[r] * w : 0.f;
             }
             const int off = (16 * J + pp) * SM::LM + 16 * I + 4 * g;
             if (!is_a)
@@ -638,7 +717,18 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                 const long orow = bh * N + r0 + row_local;
                 if (has_e) {
                     // dk(eb, J) = sum_i phi(q_i)(eb) M_ij + R(eb, :) v_j + r(eb), times phi'(k_j)
+                    // (decay: the suffix terms first, times gamma^(R - tau_j))
                     f32x4 acc = zero4;
+                    if constexpr (dec) {
+#pragma unroll
+                        for (int s = 0; s < NSV; ++s) {
+                            Frag<TC> fv;
+                            lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
+                            acc = mma(fragR[s], fv, acc);
+                            if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
+                        }
+                        acc = (acc + accr) * dcy.pow(nrows - row_local);
+                    }
 #pragma unroll
                     for (int ip = 0; ip < NTS; ++ip) {
                         if (!NC && 2 * ip + 1 >= J) {
@@ -651,22 +741,35 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                             }
                         }
                     }
+                    if constexpr (!dec) {
 #pragma unroll
-                    for (int s = 0; s < NSV; ++s) {
-                        Frag<TC> fv;
-                        lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
-                        acc = mma(fragR[s], fv, acc);
-                        if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
+                        for (int s = 0; s < NSV; ++s) {
+                            Frag<TC> fv;
+                            lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
+                            acc = mma(fragR[s], fv, acc);
+                            if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
+                        }
+                        acc = acc + accr;
                     }
                     const f32x4 kd = lds_get4(kb, 16 * J * SM::LK + 16 * eb);
                     f32x4 out;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) out[r] = (acc[r] + accr[r]) * (ident ? 1.0f : fminf(kd[r], 1.0f));
+                    for (int r = 0; r < 4; ++r) out[r] = acc[r] * (ident ? 1.0f : fminf(kd[r], 1.0f));
                     if (valid) store4<TI>(p.dk, orow * DK + 16 * eb + 4 * g, out);
                 }
                 if (has_c) {
                     // dv(cb, J) = sum_i dO_i(cb) A_ij + R^T(cb, :) phi(k_j)
+                    // (decay: the suffix term first, times gamma^(R - tau_j))
                     f32x4 acc = zero4;
+                    if constexpr (dec) {
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) {
+                            Frag<TC> fk;
+                            lds_frag_split_v(fk, kb, 16 * J * SM::LK + 32 * s);
+                            acc = mma(frt[s], fk, acc);
+                        }
+                        acc = acc * dcy.pow(nrows - row_local);
+                    }
 #pragma unroll
                     for (int ip = 0; ip < NTS; ++ip) {
                         if (!NC && 2 * ip + 1 >= J) {
@@ -675,11 +778,13 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                             acc = mma(fgt[ip], fa, acc);
                         }
                     }
+                    if constexpr (!dec) {
 #pragma unroll
-                    for (int s = 0; s < NSE; ++s) {
-                        Frag<TC> fk;
-                        lds_frag_split_v(fk, kb, 16 * J * SM::LK + 32 * s);
-                        acc = mma(frt[s], fk, acc);
+                        for (int s = 0; s < NSE; ++s) {
+                            Frag<TC> fk;
+                            lds_frag_split_v(fk, kb, 16 * J * SM::LK + 32 * s);
+                            acc = mma(frt[s], fk, acc);
+                        }
                     }
                     if (valid) store4<TI>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
                 }
@@ -690,7 +795,14 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         xk.apply_phi(ident);
         if (has_e && !NC) {
             // state carry: R^T(c', eb) += dO^T(c') (a phi(Q))(eb), r(eb) += (a phi(Q))(eb)^T e
-            // (a = 0 for token rows past the chunk)
+            // (a = 0 for token rows past the chunk; with decay the state first
+            // decays by gamma^R and query i weighs gamma^(tau_i))
+            if constexpr (dec) {
+                const float gR = dcy.pow(nrows);
+                accr = accr * gR;
+#pragma unroll
+                for (int cv = 0; cv < CV; ++cv) accR[cv] = accR[cv] * gR;
+            }
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
                 {
@@ -703,8 +815,10 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     Frag<TC> fq, fe, fe_lo;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        fq.set(t, fqt[s].get(t) * a0[t]);
-                        fq.set(t + 4, fqt[s].get(t + 4) * a1[t]);
+                        const float w0 = dec ? dcy.pow(32 * s + 4 * g + t) : 1.0f;
+                        const float w1 = dec ? dcy.pow(32 * s + 16 + 4 * g + t) : 1.0f;
+                        fq.set(t, fqt[s].get(t) * (a0[t] * w0));
+                        fq.set(t + 4, fqt[s].get(t + 4) * (a1[t] * w1));
                         fe.set(t, e0[t]);
                         fe.set(t + 4, e1[t]);
                         fe_lo.set(t, e0[t] - fe.get(t));

@@ -123,9 +123,9 @@ hipError_t run_bwd_nc_t(const BwdDesc &d) {
     }
 }
 
-template <int DK, int DV, typename TI>
-hipError_t run_bwd_t(const BwdDesc &d) {
-    if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);
+// DECAY: the causal form with a per-head decay (d.gamma non-null).
+template <int DK, int DV, typename TI, bool DECAY>
+hipError_t run_bwd_causal_t(const BwdDesc &d) {
     const long BH = (long)d.B * d.H;
     int Lmax = 0;
     const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);
@@ -144,24 +144,24 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     long target_agg = 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
         case 16:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 16, false>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false, DECAY>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 16, false, DECAY>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16, false, DECAY>();
             break;
         case 32:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 32, false>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false, DECAY>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 32, false, DECAY>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32, false, DECAY>();
             break;
         case 64:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 64, false>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false, DECAY>;
+            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 64, false, DECAY>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64, false, DECAY>();
             break;
         default: return hipErrorInvalidValue;
     }
-    auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI>;
-    auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI>;
+    auto dq_kernel = &la_bwd_dq_kernel<DK, DV, TI, false, DECAY>;
+    auto dkdv_kernel = &la_bwd_dkdv_kernel<DK, DV, TI, false, DECAY>;
     static OccCache occ_dq, occ_kv;
     const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), occ_dq, kBwdThreads);
     const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
@@ -182,6 +182,8 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     a.L = Lf;
     a.state_P = Pf;
     a.state_mult = 1;
+    a.gamma = d.gamma;
+    a.H = d.H;
     if (Pq > 1) {
         // prefix sums: the last dq segment's own fine segments are not needed
         const int nagg = (Pq - 1) * mult_q;
@@ -191,7 +193,8 @@ hipError_t run_bwd_t(const BwdDesc &d) {
         a.seg_base = 0;
         agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream)) != hipSuccess)
+        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
+            hipSuccess)
             return err;
     }
 
@@ -209,6 +212,8 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     b.phi_id = d.phi_id;
     b.C = d.C < bwd_cmax<TI, DK, DV>() ? d.C : bwd_cmax<TI, DK, DV>();
     b.state_P = Pf;
+    b.gamma = d.gamma;
+    b.H = d.H;
 
     b.state = Pq > 1 ? pre : nullptr;
     b.state_mult = mult_q;
@@ -227,7 +232,8 @@ hipError_t run_bwd_t(const BwdDesc &d) {
         a.seg_base = first;
         aggw_kernel<<<dim3((unsigned)BH, (unsigned)(Pf - first)), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, first, d.stream)) != hipSuccess)
+        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, first, d.stream, d.gamma, d.H, Lf)) !=
+            hipSuccess)
             return err;
     }
     b.state = Pkv > 1 ? suf : nullptr;
@@ -235,6 +241,12 @@ hipError_t run_bwd_t(const BwdDesc &d) {
     b.L = Pkv > 1 ? Lf * mult_kv : d.N;
     dkdv_kernel<<<dim3((unsigned)BH, (unsigned)(Pkv > 1 ? Pkv : 1)), kBwdThreads, 0, d.stream>>>(b);
     return hipGetLastError();
+}
+
+template <int DK, int DV, typename TI>
+hipError_t run_bwd_t(const BwdDesc &d) {
+    if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);
+    return d.gamma ? run_bwd_causal_t<DK, DV, TI, true>(d) : run_bwd_causal_t<DK, DV, TI, false>(d);
 }
 
 template <int DK>

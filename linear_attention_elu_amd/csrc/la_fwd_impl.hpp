@@ -86,7 +86,7 @@ struct FwdParams {
     int state_P;            // segments per (bh) in the state array
     int state_mult;         // segment s of this launch starts at state slot s * state_mult
     int seg_base;           // segment of workgroup row blockIdx.y: seg_base + blockIdx.y
-    const float *gamma;     // MODE_CAUSAL, MODE_AGG: per-head decay [H], or null for none
+    const float *gamma;     // MODE_CAUSAL, MODE_AGG(W): per-head decay [H], or null for none
     int H;                  // heads (bh % H is the head of workgroup column bh)
     int sum_P;              // MODE_APPLY: the total state is the sum of slots 0 .. sum_P - 1 (>= 1)
     int phi_id;             // feature map: 0 = elu + 1, 1 = identity (q and k are already features)
@@ -137,19 +137,9 @@ template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// g^n for an integer n (of either sign) by repeated squaring in fp32.
-__device__ __forceinline__ float powi(float g, int n) {
-    float r = 1.0f, b = g;
-    for (int e = n < 0 ? -n : n; e > 0; e >>= 1) {
-        if (e & 1) r *= b;
-        b *= b;
-    }
-    return n < 0 ? 1.0f / r : r;
-}
-
 // OBF: the output o is bf16 (else fp32).  DECAY (MODE_CAUSAL and MODE_AGG):
-// the per-head decay of p.gamma; a separate instantiation, so that the plain
-// kernels keep their registers.
+// the per-head decay of p.gamma, any value in [0, 1]; a separate
+// instantiation, so that the plain kernels keep their registers.
 template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false>
 __global__ void __launch_bounds__((fwd_threads<DK, DV, TI>()))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE>())))
@@ -200,17 +190,23 @@ la_chunk_kernel(const FwdParams p) {
     const int pp = lane & 15;
     const long bh = blockIdx.x;
     const int seg = p.seg_base + (int)blockIdx.y;
-    // Per-head decay gamma (RetNet row of the itwiki variants table), folded into
-    // the operands: with tau the row inside a chunk and m = CT / 2, phi(q) rows
-    // are staged times gamma^(tau - m) and phi(k) rows times gamma^(m - tau), so
-    // every in-chunk score carries gamma^(tau_i - tau_j); the carried state is
-    // read as gamma^(m + 1) S, and a chunk of R rows updates it to
-    // gamma^(R - 1 - m) (gamma^(m + 1) S + sum phi~(k) v^T).  The factors stay
-    // within 2^(+-(m + 1) log2(1 / gamma)), in range for gamma >= 1/4.
+    // Per-head decay gamma (RetNet row of the itwiki variants table):
+    // S_i = gamma S_{i-1} + phi(k_i) v_i^T, z likewise.  Inside a chunk every
+    // score carries gamma^(tau_i - tau_j) (tau the row in the chunk), the carried
+    // state is read as gamma^(tau_i + 1) S, and a chunk of R rows updates it to
+    // gamma^R S + sum_j gamma^(R - 1 - tau_j) phi(k_j) v_j^T.  Every factor is a
+    // power gamma^e with e >= 0, applied to MFMA results (scores, inter-chunk
+    // terms) or to the phi(k) operand of the carry, so any gamma in [0, 1] stays
+    // in range; the factors of full chunks are per-lane tables computed once.
     constexpr bool decay = DECAY && (MODE == MODE_CAUSAL || MODE == MODE_AGG);
-    const float gam = decay ? p.gamma[bh % p.H] : 1.0f;
-    constexpr int DM = CT / 2;
-    const float g_in = decay ? powi(gam, DM + 1) : 1.0f;
+    // MODE_AGGW with decay (the backward's suffix sums): token p of the segment
+    // weighs gamma^p, the sum normalised at the segment's first token; the
+    // weight joins the per-token phi(k) factor, and the sum itself is plain.
+    constexpr bool decay_w = DECAY && MODE == MODE_AGGW;
+    const float gam = (decay || decay_w) ? p.gamma[bh % p.H] : 1.0f;
+    const float lg_gam = (decay || decay_w) ? __builtin_log2f(gam) : 0.0f;  // -inf for gamma = 0
+    // gamma^e for an integer e >= 0 (gamma^0 = 1 also for gamma = 0)
+    auto gpow = [&](int e) { return e == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)e * lg_gam); };
     const int N = p.N;
     const int row_begin = seg * p.L;
     const int row_end = min(N, row_begin + p.L);
@@ -257,7 +253,11 @@ la_chunk_kernel(const FwdParams p) {
             if (weighted) rw[S] = (sid < CT && r0 + sid <= last) ? p.zw[seg_row0 + r0 + sid] : 0.f;
             if (kscaled) {
 #pragma unroll
-                for (int i = 0; i < NKS; ++i) rks[S][i] = p.kscale[seg_row0 + min(r0 + rq0 + i * RSQ, last)];
+                for (int i = 0; i < NKS; ++i) {
+                    const int row = min(r0 + rq0 + i * RSQ, last);
+                    rks[S][i] = p.kscale[seg_row0 + row];
+                    if constexpr (decay_w) rks[S][i] *= gpow(row);
+                }
             }
             if constexpr (FULL) {
                 const char *qc = qs + (long)r0 * DK * (long)sizeof(TI);
@@ -310,15 +310,6 @@ la_chunk_kernel(const FwdParams p) {
         auto load_any = [&](auto set_tag, int c) LA_INLINE { load(set_tag, Part{}, c); };
 
         // phi (times a factor) of a 16-byte vector of inputs, as a 16-byte vector of TC.
-        // decay factors of this thread's q and k vectors (rows rq0 + i RSQ of every chunk)
-        float qdec[decay ? NLQ : 1], kdec[decay ? NLQ : 1];
-#pragma unroll
-        for (int i = 0; i < NLQ; ++i) {
-            if constexpr (decay) {
-                qdec[i] = powi(gam, rq0 + i * RSQ - DM);
-                kdec[i] = powi(gam, DM - rq0 - i * RSQ);
-            }
-        }
         const bool ident = p.phi_id != 0;  // uniform: the feature map is the identity
         auto phi16 = [&](const uint4 &u, float scale) LA_INLINE {
             float x[VEC];
@@ -327,7 +318,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
             for (int t = 0; t < VEC; ++t) {
                 const float f = ident ? x[t] : phi(x[t]);
-                w.set(t, (WEIGHTED || decay) ? f * scale : f);
+                w.set(t, WEIGHTED ? f * scale : f);
             }
             if constexpr (sizeof(TC) == 2) {
                 return __builtin_bit_cast(uint4, w.v);
@@ -348,7 +339,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rq[S][i], decay ? qdec[decay ? i : 0] : 1.0f);
+                        uint4 out = phi16(rq[S][i], 1.0f);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_Q + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -358,7 +349,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
-                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : (decay ? kdec[decay ? i : 0] : 1.0f));
+                        uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : 1.0f);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;
                     }
@@ -482,22 +473,14 @@ la_chunk_kernel(const FwdParams p) {
     // all sixteen operand rows are the same vector).
     Frag<TC> fragS[CBW][NSE];
     Frag<TC> fragZ[NSE];
-    // (with decay the operands hold gamma^(m + 1) S and gamma^(m + 1) z; g_in = 1 otherwise)
     auto refresh_state_frags = [&]() LA_INLINE {
         const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NSE; ++s) {
 #pragma unroll
             for (int cs = 0; cs < CBW; ++cs)
-                if constexpr (decay)
-                    acc_to_frag(fragS[cs][s], accS[cs][2 * s] * g_in,
-                                (2 * s + 1 < NE) ? accS[cs][2 * s + 1] * g_in : zero4);
-                else
-                    acc_to_frag(fragS[cs][s], accS[cs][2 * s], (2 * s + 1 < NE) ? accS[cs][2 * s + 1] : zero4);
-            if constexpr (decay)
-                acc_to_frag(fragZ[s], accZ[2 * s] * g_in, (2 * s + 1 < NE) ? accZ[2 * s + 1] * g_in : zero4);
-            else
-                acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
+                acc_to_frag(fragS[cs][s], accS[cs][2 * s], (2 * s + 1 < NE) ? accS[cs][2 * s + 1] : zero4);
+            acc_to_frag(fragZ[s], accZ[2 * s], (2 * s + 1 < NE) ? accZ[2 * s + 1] : zero4);
         }
     };
     if (!AGGM) refresh_state_frags();
@@ -507,6 +490,37 @@ la_chunk_kernel(const FwdParams p) {
     bool diag_keep[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) diag_keep[r] = 4 * g + r <= pp;
+
+    // Decay factors, per lane (see the decay note above):
+    //   dfq[I]    inter-chunk read of query row 16 I + pp: gamma^(16 I + pp + 1);
+    //   dsc[D][r] score of key 16 J + 4g + r for query 16 I + pp, D = I - J:
+    //             gamma^(16 D + pp - 4g - r), zero above the diagonal;
+    //   dcw[s][t] carry weight of the token in slot t of token K step s of a full
+    //             chunk: gamma^(CT - 1 - token).
+    constexpr bool decay_out = decay && NEED_Q;
+    float dfq[decay_out ? NB : 1];
+    float dsc[decay_out ? NB : 1][4];
+    float dcw[decay ? NP : 1][8];
+    if constexpr (decay_out) {
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            dfq[I] = gpow(16 * I + pp + 1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = 16 * I + pp - 4 * g - r;
+                dsc[I][r] = e >= 0 ? gpow(e) : 0.0f;
+            }
+        }
+    }
+    // token of slot t in token K step s (split assignment)
+    auto slot_token = [&](int s, int t) { return 32 * s + (t < 4 ? 4 * g + t : 16 + 4 * g + t - 4); };
+    if constexpr (decay) {
+#pragma unroll
+        for (int s = 0; s < NP; ++s)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dcw[s][t] = slot_token(s, t) < CT ? gpow(CT - 1 - slot_token(s, t)) : 0.0f;
+    }
+    const float g_chunk = decay ? gpow(CT) : 1.0f;  // gamma^R for a full chunk
 
     // Store outputs of chunk c.  part = I >= 0: row block I (row 16 I + pp
     // of the chunk, columns 16 cb + 4g .. + 3) in bf16 (OBF) or fp32;
@@ -582,6 +596,7 @@ la_chunk_kernel(const FwdParams p) {
             f32x4 accD = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
+            if constexpr (decay_out) accD = accD * dfq[I];
             Frag<TC> fb[NP];  // A^T key-block pairs as B operands (split over tokens)
             if (MODE == MODE_CAUSAL) {
                 f32x4 accA[2 * NP];
@@ -594,6 +609,10 @@ la_chunk_kernel(const FwdParams p) {
                             Frag<TC> fk;  // phi(K) rows of key block J, split over features
                             lds_frag_split_at(fk, fbase[s][0], fbase[s][1], koff + 16 * J * T::LQ);
                             accA[J] = mma(fk, fq[s], accA[J]);
+                        }
+                        if constexpr (decay_out) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) accA[J][r] *= dsc[I - J][r];
                         }
                     }
                 }
@@ -613,13 +632,22 @@ la_chunk_kernel(const FwdParams p) {
             for (int cs = 0; cs < CBW; ++cs) {
                 if (col_ok(cs)) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (MODE == MODE_CAUSAL) {
+                    if constexpr (decay_out) {  // the decayed inter-chunk read first, then the chunk's own
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                        acc = acc * dfq[I];
 #pragma unroll
                         for (int jp = 0; jp < NP; ++jp)
                             if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
-                    }
+                    } else {
+                        if (MODE == MODE_CAUSAL) {
 #pragma unroll
-                    for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                            for (int jp = 0; jp < NP; ++jp)
+                                if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
+                        }
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                    }
                     outv[cs][I] = acc * inv;
                 }
             }
@@ -660,6 +688,7 @@ la_chunk_kernel(const FwdParams p) {
             f32x4 accD = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NSE; ++s) accD = mma(fragZ[s], fq[s], accD);
+            if constexpr (decay_out) accD = accD * dfq[I];
             Frag<TC> fb[NP];  // A^T key-block pairs as B operands (split over tokens)
             if constexpr (CAUSAL) {
                 // score tiles A^T(J, I) for J <= I
@@ -670,6 +699,10 @@ la_chunk_kernel(const FwdParams p) {
                     if (J <= I) {
 #pragma unroll
                         for (int s = 0; s < NSE; ++s) accA[J] = mma(fk[J][s], fq[s], accA[J]);
+                        if constexpr (decay_out) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) accA[J][r] *= dsc[I - J][r];
+                        }
                     }
                 }
 #pragma unroll
@@ -688,13 +721,22 @@ la_chunk_kernel(const FwdParams p) {
             for (int cs = 0; cs < CBW; ++cs) {
                 if (col_ok(cs)) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (CAUSAL) {
+                    if constexpr (decay_out) {  // the decayed inter-chunk read first, then the chunk's own
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                        acc = acc * dfq[I];
 #pragma unroll
                         for (int jp = 0; jp < NP; ++jp)
                             if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
-                    }
+                    } else {
+                        if constexpr (CAUSAL) {
 #pragma unroll
-                    for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                            for (int jp = 0; jp < NP; ++jp)
+                                if (2 * jp <= I) acc = mma(fvt[cs][jp], fb[jp], acc);
+                        }
+#pragma unroll
+                        for (int s = 0; s < NSE; ++s) acc = mma(fragS[cs][s], fq[s], acc);
+                    }
                     outv[cs][I] = acc * inv;
                 }
             }
@@ -721,13 +763,16 @@ la_chunk_kernel(const FwdParams p) {
         store(-1, outv, den);
 
         // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
+        // (decay: S = gamma^R S + sum_j gamma^(R - 1 - tau_j) phi(k_j) v_j^T, the
+        // weights applied to the phi(K) operand)
         if constexpr (decay) {
             if (NEED_K && has_cols) {
+                const float gR = crows == CT ? g_chunk : gpow(crows);
 #pragma unroll
                 for (int E = 0; E < NE; ++E) {
-                    accZ[E] = accZ[E] * g_in;
+                    accZ[E] = accZ[E] * gR;
 #pragma unroll
-                    for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_in;
+                    for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * gR;
                 }
             }
         }
@@ -747,9 +792,20 @@ la_chunk_kernel(const FwdParams p) {
                         fw_lo.set(t, x - fw.get(t));
                     }
                 }
+                float cw[decay ? 8 : 1];  // carry weights of this step's tokens
+                if constexpr (decay) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        cw[t] = crows == CT ? dcw[s][t]
+                                            : (slot_token(s, t) < crows ? gpow(crows - 1 - slot_token(s, t)) : 0.0f);
+                }
 #pragma unroll
                 for (int E = 0; E < NE; ++E) {
                     lds_frag_tr(fkt[E], sk, T::LQ, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * E, pp);
+                    if constexpr (decay) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) fkt[E].set(t, fkt[E].get(t) * cw[t]);
+                    }
                     accZ[E] = mma(fkt[E], fw, accZ[E]);
                     if (weighted && sizeof(TC) == 2) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
                 }
@@ -762,15 +818,6 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
                         for (int E = 0; E < NE; ++E) accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
                     }
-                }
-                    }
-            if constexpr (decay) {
-                const float g_out = powi(gam, crows - 1 - DM);
-#pragma unroll
-                for (int E = 0; E < NE; ++E) {
-                    accZ[E] = accZ[E] * g_out;
-#pragma unroll
-                    for (int cs = 0; cs < CBW; ++cs) accS[cs][E] = accS[cs][E] * g_out;
                 }
             }
             if (MODE == MODE_CAUSAL) refresh_state_frags();

@@ -49,6 +49,7 @@ struct BwdDesc {
     hipStream_t stream;
     int noncausal;  // gradient of the non-causal form (full sums)
     int phi_id;     // feature map: 0 = elu + 1, 1 = identity
+    const float *gamma;  // causal only: per-head decay [H] (device), or null for none
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a
@@ -78,8 +79,9 @@ inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 // mode 1 writes the total of all P slots into slot 0; mode 2 replaces slots
 // [lim, P) by their exclusive suffix and writes the sum of all of them into
 // slot lim - 1 (when lim > 0).  Other slots are not touched.  Fixed order.
-// With gamma non-null (mode 0), the segments hold L tokens each and decay by
-// gamma[bh % H] per token: entering(s) = gamma^L entering(s - 1) + aggregate(s - 1).
+// With gamma non-null, the segments hold L tokens each and decay by
+// gamma[bh % H] per token: mode 0, entering(s) = gamma^L entering(s - 1) +
+// aggregate(s - 1); mode 2, after(s) = aggregate(s + 1) + gamma^L after(s + 1).
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
                            int mode, int lim, hipStream_t stream, const float *gamma = nullptr, int H = 1,
                            int L = 0);

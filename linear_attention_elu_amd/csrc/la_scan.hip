@@ -20,9 +20,12 @@ namespace la {
 //           [max(lim - 1, 0), P) are written.
 // Slots outside those ranges are neither read nor written, so a caller
 // aggregates only the segments whose sums some later pass reads.
-// With a per-head decay (gamma non-null, mode 0) every segment holds L
-// tokens and its aggregate is taken at its last token, so the state entering
-// segment s is gamma^L times the state entering s - 1 plus the aggregate of s - 1.
+// With a per-head decay (gamma non-null) every segment holds L tokens.  Mode
+// 0: an aggregate is taken at its segment's last token, so the state entering
+// segment s is gamma^L times the state entering s - 1 plus the aggregate of
+// s - 1.  Mode 2: an aggregate is normalised at its segment's first token, so
+// the suffix after segment s is the aggregate of s + 1 plus gamma^L times the
+// suffix after s + 1.
 static __global__ void __launch_bounds__(256)
 la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode, int lim,
                    const float *gamma, int H, int L) {
@@ -31,15 +34,15 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
     const int idx = blockIdx.y * 256 + threadIdx.x;
     if (idx >= SS) return;
     float *base = ws + bh * (long)P * SS + idx;
-    if (mode == 0) {
-        float f = 1.0f;  // gamma^L by repeated squaring
-        if (gamma) {
-            float b = gamma[bh % H];
-            for (int e = L; e > 0; e >>= 1) {
-                if (e & 1) f *= b;
-                b *= b;
-            }
+    float f = 1.0f;  // gamma^L by repeated squaring
+    if (gamma) {
+        float b = gamma[bh % H];
+        for (int e = L; e > 0; e >>= 1) {
+            if (e & 1) f *= b;
+            b *= b;
         }
+    }
+    if (mode == 0) {
         float run = 0.f;
         if (idx < DK * DV) {
             if (S0) run = S0[bh * (long)DK * DV + idx];
@@ -61,7 +64,7 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
         for (int s = P - 1; s >= lim; --s) {
             const float a = base[(long)s * SS];
             base[(long)s * SS] = run;
-            run += a;
+            run = gamma ? a + f * run : run + a;
         }
         if (lim > 0) base[(long)(lim - 1) * SS] = run;
     }

@@ -234,6 +234,24 @@ def test_feature_map_entry_points_reject(lib):
     assert h(*([P] * 7), 2, P, 64, 1, 1, 64, 64, 64, 64, 1, P, 16, None) == 5
 
 
+def test_bwd_causal_decay_rejects(lib):
+    f = lib.la_bwd_causal_decay
+    need = la.la_bwd_causal_workspace_bytes(1, 1, 64, 64, 64, 64)
+    args = [P] * 8 + [1, 1, 64, 64, 64, 64, 1, P, need, None]
+    bad = list(args)
+    bad[7] = None  # gamma
+    assert f(*bad) == 1
+    bad = list(args)
+    bad[7] = 0x1002  # gamma not 4-byte aligned
+    assert f(*bad) == 7
+    bad = list(args)
+    bad[13] = 8  # C
+    assert f(*bad) == 3
+    bad = list(args)
+    bad[-2] = need - 1
+    assert f(*bad) == 5
+
+
 def test_decode_decay_rejects(lib):
     f = lib.la_decode_step_decay
     assert f(P, P, P, P, P, P, None, 1, 1, 32, 32, 0, None) == 1
