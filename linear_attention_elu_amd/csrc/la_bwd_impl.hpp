@@ -78,6 +78,8 @@ struct BwdParams {
     int phi_id;              // feature map: 0 = elu + 1, 1 = identity (phi' = 1)
     const float *gamma;      // DECAY: per-head decay [H]
     int H;                   // heads (bh % H is the head of workgroup column bh)
+    float *suf_out;          // causal dq sweep: per (bh, segment) suffix sums of its segment, or null
+    int suf_P;               // segments per bh in suf_out
 };
 
 // Per-head decay (itwiki "선형 어텐션", table of later variants, RetNet row):
@@ -184,7 +186,11 @@ __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
 }
 
 // ---------------------------------------------------------------------------
-// dq sweep (forward over chunks, state S, z).
+// dq sweep (forward over chunks, state S, z).  It also forms, once a chunk's
+// a = 1 / den and e = eps * den are known, its segment's share of the dk/dv
+// sweep's suffix state: R_seg = sum_i (phi(q_i) a_i) g_i^T and
+// r_seg = sum_i (phi(q_i) a_i) e_i over the segment (token p of the segment
+// weighs gamma^p with a decay), so no separate pass re-reads q and dO.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, typename TI, bool DEC = false> struct DqSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
@@ -266,6 +272,13 @@ la_bwd_dq_kernel(const BwdParams p) {
                 for (int r = 0; r < 4; ++r) accS[cv][r] += Sin[(16 * eb + pp) * DV + 16 * cv + 4 * g + r];
         }
     }
+    // this segment's suffix sums (segment 0's are never read): R^T(c', eb) tiles,
+    // lane (pp, g) holding R[16 eb + pp][16 c' + 4g + r], and r(eb) as r[16 eb + 4g + r]
+    const bool suf = !NC && p.suf_out != nullptr && seg > 0;  // uniform
+    f32x4 accRs[NC ? 1 : CV];
+    f32x4 accrs = zero4;
+#pragma unroll
+    for (int cv = 0; cv < (NC ? 1 : CV); ++cv) accRs[cv] = zero4;
     Frag<TC> fragS[NSV];  // S rows e, split over the value index
     // Non-causal, or decayed, with bf16 operands: S also as its rounding
     // remainder, so that X = S g and z meet at fp32-level accuracy in
@@ -434,6 +447,9 @@ la_bwd_dq_kernel(const BwdParams p) {
             }
         }
         __syncthreads();  // partial dot products of every wave are in LDS
+        float a_row[NIB], e_row[NIB];  // a and e of query 16 I + pp
+#pragma unroll
+        for (int I = 0; I < NIB; ++I) a_row[I] = e_row[I] = 0.f;
         if (active) {
 #pragma unroll
             for (int I = 0; I < NIB; ++I) {
@@ -453,12 +469,56 @@ la_bwd_dq_kernel(const BwdParams p) {
                         p.inv_den[orow] = inv;
                         p.eps[orow] = -coef;
                     }
+                    a_row[I] = valid ? inv : 0.f;  // every lane group holds its rows' values
+                    e_row[I] = valid ? -coef : 0.f;
                     const f32x4 fq = lds_get4(qb, 16 * I * SM::LQ);
                     f32x4 out;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         out[r] = (X[I][r] - Z[I][r] * coef) * inv * (ident ? 1.0f : fminf(fq[r], 1.0f));
                     if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
+                }
+            }
+        }
+        if constexpr (!NC) {
+            if (suf && active) {
+                {
+                    // R_seg^T(c', eb) += dO^T(c') (w a phi(Q))(eb), r_seg(eb) += (w a phi(Q))(eb)^T e,
+                    // w = gamma^(position in the segment) (1 without decay).  The
+                    // operands run over tokens: slot t of lane group g is token
+                    // 32 s + 4g + t (+16), whose a and e lane 4g + t holds.
+#pragma unroll
+                    for (int s = 0; s < NTS; ++s) {
+                        f32x4 a0, a1, e0, e1;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            a0[t] = __shfl(a_row[2 * s], 4 * g + t, 64);
+                            a1[t] = __shfl(a_row[2 * s + 1], 4 * g + t, 64);
+                            e0[t] = __shfl(e_row[2 * s], 4 * g + t, 64);
+                            e1[t] = __shfl(e_row[2 * s + 1], 4 * g + t, 64);
+                        }
+                        Frag<TC> fqt, fq, fe, fe_lo;
+                        lds_frag_tr(fqt, sm.q, SM::LQ, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * eb, pp);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const float w0 = dec ? dcy.pow(ch * C + 32 * s + 4 * g + t) : 1.0f;
+                            const float w1 = dec ? dcy.pow(ch * C + 32 * s + 16 + 4 * g + t) : 1.0f;
+                            fq.set(t, fqt.get(t) * (a0[t] * w0));
+                            fq.set(t + 4, fqt.get(t + 4) * (a1[t] * w1));
+                            fe.set(t, e0[t]);
+                            fe.set(t + 4, e1[t]);
+                            fe_lo.set(t, e0[t] - fe.get(t));
+                            fe_lo.set(t + 4, e1[t] - fe.get(t + 4));
+                        }
+                        accrs = mma(fq, fe, accrs);
+                        if constexpr (SM::LO) accrs = mma(fq, fe_lo, accrs);
+#pragma unroll
+                        for (int cv = 0; cv < CV; ++cv) {
+                            Frag<TC> fgc;
+                            lds_frag_tr(fgc, sm.g, SM::LG, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
+                            accRs[cv] = mma(fgc, fq, accRs[cv]);
+                        }
+                    }
                 }
             }
         }
@@ -493,6 +553,19 @@ la_bwd_dq_kernel(const BwdParams p) {
                 }
             }
             refresh();
+        }
+    }
+    if constexpr (!NC) {
+        if (suf && active) {
+            float *Rs = p.suf_out + (bh * p.suf_P + seg) * (long)(DK * DV + DK);
+#pragma unroll
+            for (int cv = 0; cv < CV; ++cv)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Rs[(16 * eb + pp) * DV + 16 * cv + 4 * g + r] = accRs[cv][r];
+            if (pp == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Rs[DK * DV + 16 * eb + 4 * g + r] = accrs[r];
+            }
         }
     }
 }

@@ -2,7 +2,8 @@
 //
 //   [P > 1]     aggregates of phi(K)^T V, phi(K)^T 1 per segment -> exclusive prefix
 //   dq sweep    forward over the chunks of every segment; leaves 1/den and eps
-//   [P > 1]     aggregates of (phi(Q)/den)^T dO, (phi(Q)/den)^T e -> exclusive suffix
+//               per token and each segment's (phi(Q)/den)^T dO, (phi(Q)/den)^T e
+//   [P > 1]     exclusive suffix over the segments
 //   dk/dv sweep backward over the chunks of every segment
 #pragma once
 
@@ -140,22 +141,18 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     // The aggregate passes reuse the forward's chunk kernel at the caller's
     // chunk size: plain for the prefix sums, weighted for the suffix sums.
     void (*agg_kernel)(const FwdParams) = nullptr;
-    void (*aggw_kernel)(const FwdParams) = nullptr;
     long target_agg = 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
         case 16:
             agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false, DECAY>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 16, false, DECAY>;
             target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16, false, DECAY>();
             break;
         case 32:
             agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false, DECAY>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 32, false, DECAY>;
             target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32, false, DECAY>();
             break;
         case 64:
             agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false, DECAY>;
-            aggw_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGGW, 64, false, DECAY>;
             target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64, false, DECAY>();
             break;
         default: return hipErrorInvalidValue;
@@ -172,9 +169,11 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
         *mult = (int)((Pf + want - 1) / want);
         return (Pf + *mult - 1) / *mult;
     };
-    int mult_q = 1, mult_kv = 1;
-    const int Pq = split(target_dq, &mult_q);
-    const int Pkv = split(target_kv, &mult_kv);
+    // One split for both sweeps: the dq sweep leaves each segment's suffix sums
+    // for the dk/dv sweep's segments.
+    int mult = 1;
+    const int Pc = split(target_dq < target_kv ? target_dq : target_kv, &mult);
+    const int Lc = Lf * mult;
 
     FwdParams a{};
     a.N = d.N;
@@ -184,9 +183,9 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     a.state_mult = 1;
     a.gamma = d.gamma;
     a.H = d.H;
-    if (Pq > 1) {
-        // prefix sums: the last dq segment's own fine segments are not needed
-        const int nagg = (Pq - 1) * mult_q;
+    if (Pc > 1) {
+        // prefix sums: the last segment's own fine segments are not needed
+        const int nagg = (Pc - 1) * mult;
         a.k = d.k;
         a.v = d.v;
         a.seg_out = pre;
@@ -215,31 +214,28 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     b.gamma = d.gamma;
     b.H = d.H;
 
-    b.state = Pq > 1 ? pre : nullptr;
-    b.state_mult = mult_q;
-    b.L = Pq > 1 ? Lf * mult_q : d.N;
-    dq_kernel<<<dim3((unsigned)BH, (unsigned)(Pq > 1 ? Pq : 1)), kBwdThreads, 0, d.stream>>>(b);
+    // dq sweep: reads the prefix states at fine slots, writes each segment's
+    // suffix sums to slot [bh][segment] of `suf` (segments 1 .. Pc - 1)
+    b.state = Pc > 1 ? pre : nullptr;
+    b.state_mult = mult;
+    b.L = Pc > 1 ? Lc : d.N;
+    b.suf_out = Pc > 1 ? suf : nullptr;
+    b.suf_P = Pc;
+    dq_kernel<<<dim3((unsigned)BH, (unsigned)Pc), kBwdThreads, 0, d.stream>>>(b);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
-    if (Pkv > 1) {
-        a.k = d.q;  // (a phi(Q))^T dO and (a phi(Q))^T e, a = 1 / den
-        a.v = d.dO;
-        a.kscale = inv_den;
-        a.zw = eps;
-        a.seg_out = suf;
-        // suffix sums: the first dk/dv segment's own fine segments are not needed
-        const int first = mult_kv;
-        a.seg_base = first;
-        aggw_kernel<<<dim3((unsigned)BH, (unsigned)(Pf - first)), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pf, DK, DV, 2, first, d.stream, d.gamma, d.H, Lf)) !=
+    if (Pc > 1) {
+        // exclusive suffix over the segments: slot s receives the sums after segment s
+        if ((err = launch_seg_scan(suf, nullptr, nullptr, BH, Pc, DK, DV, 2, 1, d.stream, d.gamma, d.H, Lc)) !=
             hipSuccess)
             return err;
     }
-    b.state = Pkv > 1 ? suf : nullptr;
-    b.state_mult = mult_kv;
-    b.L = Pkv > 1 ? Lf * mult_kv : d.N;
-    dkdv_kernel<<<dim3((unsigned)BH, (unsigned)(Pkv > 1 ? Pkv : 1)), kBwdThreads, 0, d.stream>>>(b);
+    b.suf_out = nullptr;
+    b.state = Pc > 1 ? suf : nullptr;
+    b.state_P = Pc;
+    b.state_mult = 1;
+    b.L = Pc > 1 ? Lc : d.N;
+    dkdv_kernel<<<dim3((unsigned)BH, (unsigned)Pc), kBwdThreads, 0, d.stream>>>(b);
     return hipGetLastError();
 }
 
