@@ -72,7 +72,7 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     a.k = d.k;
     a.v = d.v;
     a.seg_out = tot;
-    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI, MODE_AGG>(), 0, d.stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     BwdParams b{};
@@ -105,7 +105,7 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     a.kscale = inv_den;
     a.zw = eps;
     a.seg_out = rtot;
-    aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+    aggw_kernel<<<dim3((unsigned)BH, (unsigned)Pf), fwd_threads<DK, DV, TI, MODE_AGGW>(), 0, d.stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 
     b.state = rtot;
@@ -190,7 +190,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
         a.v = d.v;
         a.seg_out = pre;
         a.seg_base = 0;
-        agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(a);
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI, MODE_AGG, DECAY>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
             hipSuccess)

@@ -6,7 +6,8 @@
 //                  carried into the segment;
 //   MODE_APPLY  -- the non-causal read-out phi(Q) S / phi(Q) z with a fixed state;
 //   MODE_AGGW   -- MODE_AGG with a per-token factor on each phi(k) row and
-//                  per-token weights in the z sum (the backward's suffix sums).
+//                  per-token weights in the z sum (the non-causal backward's
+//                  total of (phi(q) / den)^T [dO, -eps]).
 // Chunked causal form (itwiki "선형 어텐션", table "Comparison of forms", chunked
 // row, and section "Implementation"): inside a chunk of C tokens the causal
 // scores are a masked matrix product, between chunks the state
@@ -27,10 +28,12 @@
 //     with the gfx950 transpose read (ds_read_b64_tr_b16) where it runs over
 //     tokens -- run the MFMA work and store the outputs.
 // The tiles are double buffered: while the compute waves work on chunk c the
-// staging waves fill chunk c + 1, with a single barrier per chunk.  Wider
-// heads and fp32, whose compute waves need more registers than two waves per
-// SIMD leave, use four waves that do both jobs in turn (stage chunk c + 1,
-// compute chunk c) with one register set.  Chunks
+// staging waves fill chunk c + 1, with a single barrier per chunk.  The
+// aggregate passes (no outputs) use the same split layout at d = 128 too, one
+// workgroup per CU.  Wider heads in the causal and read-out passes, and fp32,
+// whose compute waves need more registers than two waves per SIMD leave, use
+// four waves that do both jobs in turn (stage chunk c + 1, compute chunk c)
+// with one register set.  Chunks
 // whose rows are all valid run an unrolled loop (buffer and register-set
 // indices are constants) with fixed per-lane offsets from a uniform base and
 // no row masks; the last chunks run a general loop with clamped loads.
@@ -58,13 +61,21 @@ enum { MODE_AGG = 0, MODE_CAUSAL = 1, MODE_APPLY = 2, MODE_AGGW = 3 };
 constexpr int kRoleThreads = 256;  // four waves per role
 
 // Separate staging and compute waves (eight per workgroup) where the compute
-// waves fit in the registers two waves per SIMD leave; otherwise four waves
-// take both roles.
-template <int DK, int DV, typename TI> constexpr bool fwd_split() {
-    return sizeof(TI) == 2 && DK <= 64 && DV <= 64;
+// waves fit in the registers two waves per SIMD leave: bf16 with d_k, d_v <=
+// 64, and the aggregate passes without decay (no outputs: their compute waves
+// hold only the state) at every width; otherwise four waves take both roles.
+// At d = 128, B=8, H=16, N=8192 the split aggregate took 77 us where four
+// waves took 105; with decay its tables spill and four waves were faster.
+template <int DK, int DV, typename TI, int MODE = MODE_CAUSAL, bool DECAY = false> constexpr bool fwd_split() {
+    return sizeof(TI) == 2 && ((DK <= 64 && DV <= 64) || ((MODE == MODE_AGG || MODE == MODE_AGGW) && !DECAY));
 }
-template <int DK, int DV, typename TI> constexpr int fwd_threads() {
-    return fwd_split<DK, DV, TI>() ? 2 * kRoleThreads : kRoleThreads;
+template <int DK, int DV, typename TI, int MODE = MODE_CAUSAL, bool DECAY = false> constexpr int fwd_threads() {
+    return fwd_split<DK, DV, TI, MODE, DECAY>() ? 2 * kRoleThreads : kRoleThreads;
+}
+// A wide aggregate pass (d_k or d_v of 128) in the split layout: one
+// workgroup per CU (its compute waves hold a 128-wide state).
+template <int DK, int DV, typename TI, int MODE, bool DECAY> constexpr bool fwd_wide_agg() {
+    return fwd_split<DK, DV, TI, MODE, DECAY>() && (MODE == MODE_AGG || MODE == MODE_AGGW) && (DK > 64 || DV > 64);
 }
 
 struct FwdParams {
@@ -86,7 +97,7 @@ struct FwdParams {
     int state_P;            // segments per (bh) in the state array
     int state_mult;         // segment s of this launch starts at state slot s * state_mult
     int seg_base;           // segment of workgroup row blockIdx.y: seg_base + blockIdx.y
-    const float *gamma;     // MODE_CAUSAL, MODE_AGG(W): per-head decay [H], or null for none
+    const float *gamma;     // MODE_CAUSAL, MODE_AGG: per-head decay [H], or null for none
     int H;                  // heads (bh % H is the head of workgroup column bh)
     int sum_P;              // MODE_APPLY: the total state is the sum of slots 0 .. sum_P - 1 (>= 1)
     int phi_id;             // feature map: 0 = elu + 1, 1 = identity (q and k are already features)
@@ -95,7 +106,7 @@ struct FwdParams {
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
 // reads are allocated.  Byte offsets inside one buffer: q, k, v, then the
 // per-token z weights.
-template <int DK, int DV, typename TC, int CT, int MODE> struct FwdTiles {
+template <int DK, int DV, typename TC, int CT, int MODE, bool DECAY = false> struct FwdTiles {
     static constexpr int DKP = DK < 32 ? 32 : DK;        // feature dim padded to a K step
     // Row padding, in elements, against LDS bank conflicts (64 banks of 4
     // bytes; a 64-lane 8-byte read is served 32 lanes per cycle): 16 bytes
@@ -115,15 +126,17 @@ template <int DK, int DV, typename TC, int CT, int MODE> struct FwdTiles {
     static constexpr int BUF = QB + KB + VB + WB;          // bytes per buffer (multiple of 16)
     // Double buffering where it leaves room: a split workgroup has its CU's
     // LDS to itself; four-wave workgroups keep the buffers small.
-    static constexpr int NBUF = 2 * BUF <= (fwd_split<DK, DV, TC>() ? 150 : 64) * 1024 ? 2 : 1;
+    static constexpr int NBUF = 2 * BUF <= (fwd_split<DK, DV, TC, MODE, DECAY>() ? 150 : 64) * 1024 ? 2 : 1;
 };
 
 // Waves per SIMD the compiler must leave room for (registers are split among
 // them).  A split workgroup puts two waves on every SIMD; its causal chunk
 // loop needs the registers of one workgroup per CU, its aggregate and
 // read-out passes fit two.  Four-wave workgroups get all registers.
-template <int DK, int DV, typename TI, int CT, int MODE> constexpr int fwd_waves_per_eu() {
-    return fwd_split<DK, DV, TI>() ? (MODE != MODE_CAUSAL ? 4 : 2) : 1;
+template <int DK, int DV, typename TI, int CT, int MODE, bool DECAY> constexpr int fwd_waves_per_eu() {
+    return fwd_split<DK, DV, TI, MODE, DECAY>()
+               ? ((MODE == MODE_CAUSAL || fwd_wide_agg<DK, DV, TI, MODE, DECAY>()) ? 2 : 4)
+               : 1;
 }
 
 #define LA_INLINE __attribute__((always_inline))
@@ -141,13 +154,13 @@ template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
 // the per-head decay of p.gamma, any value in [0, 1]; a separate
 // instantiation, so that the plain kernels keep their registers.
 template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false>
-__global__ void __launch_bounds__((fwd_threads<DK, DV, TI>()))
-__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE>())))
+__global__ void __launch_bounds__((fwd_threads<DK, DV, TI, MODE, DECAY>()))
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE, DECAY>())))
 la_chunk_kernel(const FwdParams p) {
     using TC = TI;  // matrix operands keep the input precision
-    using T = FwdTiles<DK, DV, TC, CT, MODE>;
-    constexpr bool SPLIT = fwd_split<DK, DV, TI>();
-    constexpr int kThreads = fwd_threads<DK, DV, TI>();
+    using T = FwdTiles<DK, DV, TC, CT, MODE, DECAY>;
+    constexpr bool SPLIT = fwd_split<DK, DV, TI, MODE, DECAY>();
+    constexpr int kThreads = fwd_threads<DK, DV, TI, MODE, DECAY>();
     constexpr int NBUF = T::NBUF;
     // Register sets of the staging waves, i.e. chunks loaded ahead.  The
     // causal chunk loop runs one workgroup per CU and its staging waves have
@@ -198,13 +211,10 @@ la_chunk_kernel(const FwdParams p) {
     // power gamma^e with e >= 0, applied to MFMA results (scores, inter-chunk
     // terms) or to the phi(k) operand of the carry, so any gamma in [0, 1] stays
     // in range; the factors of full chunks are per-lane tables computed once.
-    constexpr bool decay = DECAY && (MODE == MODE_CAUSAL || MODE == MODE_AGG);
-    // MODE_AGGW with decay (the backward's suffix sums): token p of the segment
-    // weighs gamma^p, the sum normalised at the segment's first token; the
-    // weight joins the per-token phi(k) factor, and the sum itself is plain.
-    constexpr bool decay_w = DECAY && MODE == MODE_AGGW;
-    const float gam = (decay || decay_w) ? p.gamma[bh % p.H] : 1.0f;
-    const float lg_gam = (decay || decay_w) ? __builtin_log2f(gam) : 0.0f;  // -inf for gamma = 0
+    static_assert(!DECAY || MODE == MODE_CAUSAL || MODE == MODE_AGG, "decay: causal chunk loop and its aggregate");
+    constexpr bool decay = DECAY;
+    const float gam = decay ? p.gamma[bh % p.H] : 1.0f;
+    const float lg_gam = decay ? __builtin_log2f(gam) : 0.0f;  // -inf for gamma = 0
     // gamma^e for an integer e >= 0 (gamma^0 = 1 also for gamma = 0)
     auto gpow = [&](int e) { return e == 0 ? 1.0f : __builtin_amdgcn_exp2f((float)e * lg_gam); };
     const int N = p.N;
@@ -256,7 +266,6 @@ la_chunk_kernel(const FwdParams p) {
                 for (int i = 0; i < NKS; ++i) {
                     const int row = min(r0 + rq0 + i * RSQ, last);
                     rks[S][i] = p.kscale[seg_row0 + row];
-                    if constexpr (decay_w) rks[S][i] *= gpow(row);
                 }
             }
             if constexpr (FULL) {

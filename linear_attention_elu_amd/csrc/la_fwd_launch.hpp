@@ -15,7 +15,7 @@ template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool 
 long chunk_resident() {
     static OccCache cache;
     return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY>),
-                               cache, fwd_threads<DK, DV, TI>());
+                               cache, fwd_threads<DK, DV, TI, MODE, DECAY>());
 }
 
 // Aggregate segments per (b, h) of the non-causal form (at most).  At B=4,
@@ -73,7 +73,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
             p.seg_out = d.ws;
             p.L = Lf;
             p.state_mult = 1;
-            agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+            agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI, MODE_AGG, DECAY>(), 0, d.stream>>>(p);
             if ((err = hipGetLastError()) != hipSuccess) return err;
             if ((err = launch_seg_scan(d.ws, d.S0, d.z0, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
                 hipSuccess)
@@ -81,12 +81,12 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
             p.seg_state = d.ws;
             p.state_mult = mult;
             p.L = Lf * mult;
-            main_kernel<<<dim3((unsigned)BH, (unsigned)Pm), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+            main_kernel<<<dim3((unsigned)BH, (unsigned)Pm), fwd_threads<DK, DV, TI, MODE_CAUSAL, DECAY>(), 0, d.stream>>>(p);
         } else {
             p.S0 = d.S0;
             p.z0 = d.z0;
             p.L = d.N;
-            main_kernel<<<dim3((unsigned)BH, 1u), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+            main_kernel<<<dim3((unsigned)BH, 1u), fwd_threads<DK, DV, TI, MODE_CAUSAL, DECAY>(), 0, d.stream>>>(p);
         }
         return hipGetLastError();
     }
@@ -102,7 +102,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.L = Ln;
     p.state_P = Pn;
     p.state_mult = 1;
-    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pn), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+    agg_kernel<<<dim3((unsigned)BH, (unsigned)Pn), fwd_threads<DK, DV, TI, MODE_AGG>(), 0, d.stream>>>(p);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // The read-out is independent per row: split it on its own.
     int La = 0;
@@ -110,7 +110,7 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.seg_state = d.ws;
     p.sum_P = Pn;
     p.L = La;
-    main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), fwd_threads<DK, DV, TI>(), 0, d.stream>>>(p);
+    main_kernel<<<dim3((unsigned)BH, (unsigned)Pa), fwd_threads<DK, DV, TI, MODE_APPLY>(), 0, d.stream>>>(p);
     return hipGetLastError();
 }
 
