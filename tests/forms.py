@@ -6,12 +6,13 @@ map taken from the library ELU (torch.nn.functional.elu on the CPU in
 float64) rather than the oracle's own branch.  Sources, by page and section:
 
 - quadratic causal form: itwiki '선형 어텐션', table 'Comparison of forms'
-  (parallel form, masked matrix product) and section 'Implementation';
+  (parallel form: the causally masked pair weights);
 - non-causal form, phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1): velog review
   section 3.2; blog digest 'Method / key components 2)';
 - chunked form (matrix product inside a chunk, state passed between chunks,
-  ragged last chunk): itwiki table 'Comparison of forms' (chunked row) and
-  section 'Implementation'.
+  ragged last chunk): itwiki table 'Comparison of forms' (chunked row).  It is
+  evaluated here for all chunks at once (chunk sums, then an exclusive prefix
+  over chunks), not as a loop over chunks.
 """
 from __future__ import annotations
 
@@ -26,12 +27,14 @@ def phi(x: np.ndarray) -> np.ndarray:
 
 
 def causal_quadratic(q, k, v):
-    """[..., N, dk], [..., N, dk], [..., N, dv] -> (out, den)."""
+    """[..., N, dk], [..., N, dk], [..., N, dv] -> (out, den).  Every pair
+    weight phi(q_i) . phi(k_j), kept where key j does not come after query i."""
     fq, fk = phi(q), phi(k)
-    N = q.shape[-2]
-    a = np.matmul(fq, np.swapaxes(fk, -1, -2)) * np.tril(np.ones((N, N)))
-    den = a.sum(-1)
-    return np.matmul(a, v) / den[..., None], den
+    pos = np.arange(q.shape[-2])
+    keep = np.greater_equal.outer(pos, pos).astype(np.float64)
+    w = np.einsum("...ie,...je->...ij", fq, fk) * keep
+    den = w.sum(-1)
+    return np.einsum("...ij,...jc->...ic", w, v) / den[..., None], den
 
 
 def causal_quadratic_decay(q, k, v, gamma):
@@ -62,23 +65,27 @@ def noncausal_associative(q, k, v):
 
 
 def causal_chunked(q, k, v, C):
-    fq, fk = phi(q), phi(k)
+    """The chunked form evaluated for all chunks at once: the sequence is padded
+    to whole chunks (padded keys get phi = 0, so they add nothing), every chunk's
+    sums phi(K_c)^T [V_c, 1] are formed together, an exclusive prefix over the
+    chunk axis gives each chunk's entering state, and the in-chunk part is a
+    masked product inside each chunk."""
     lead = q.shape[:-2]
     N, dk = q.shape[-2:]
-    dv = v.shape[-1]
-    S = np.zeros(lead + (dk, dv))
-    z = np.zeros(lead + (dk,))
-    outs = []
-    for s in range(0, N, C):
-        qc, kc, vc = fq[..., s:s + C, :], fk[..., s:s + C, :], v[..., s:s + C, :]
-        n = qc.shape[-2]
-        intra = np.matmul(qc, np.swapaxes(kc, -1, -2)) * np.tril(np.ones((n, n)))
-        num = np.matmul(qc, S) + np.matmul(intra, vc)
-        den = np.matmul(qc, z[..., None])[..., 0] + intra.sum(-1)
-        outs.append(num / den[..., None])
-        S = S + np.matmul(np.swapaxes(kc, -1, -2), vc)
-        z = z + kc.sum(-2)
-    return np.concatenate(outs, axis=-2)
+    nc = -(-N // C)
+    pad = [(0, 0)] * len(lead) + [(0, nc * C - N), (0, 0)]
+    fq = np.pad(phi(q), pad).reshape(lead + (nc, C, dk))
+    fk = np.pad(phi(k), pad).reshape(lead + (nc, C, dk))
+    va = np.concatenate([v, np.ones(v.shape[:-1] + (1,))], axis=-1)   # [v, 1]: numerator and normaliser
+    va = np.pad(va, pad).reshape(lead + (nc, C, va.shape[-1]))
+    sums = np.einsum("...ctd,...ctx->...cdx", fk, va)                    # per chunk phi(K_c)^T [V_c, 1]
+    entering = np.cumsum(sums, axis=-3) - sums                         # sum over earlier chunks
+    pos = np.arange(C)
+    keep = np.greater_equal.outer(pos, pos).astype(np.float64)
+    w = np.einsum("...cid,...cjd->...cij", fq, fk) * keep
+    both = np.einsum("...cij,...cjx->...cix", w, va) + np.einsum("...cid,...cdx->...cix", fq, entering)
+    both = both.reshape(lead + (nc * C, both.shape[-1]))[..., :N, :]
+    return both[..., :-1] / both[..., -1:]
 
 
 def fd_gradient(f, x, h=1e-6):

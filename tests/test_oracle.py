@@ -22,11 +22,12 @@ def test_fp32_forms_agree_with_oracle_at_demo_shapes(oracle_lib):
     k = r.standard_normal((2, 1, 50, 16)).astype(np.float32)
     v = r.standard_normal((2, 1, 50, 32)).astype(np.float32)
     o64, _ = oracle_lib.fwd_causal(q, k, v)
+    # fp32 pair weights, each query against the keys up to its own position
     tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
-    fq = torch.nn.functional.elu(tq) + 1
-    fk = torch.nn.functional.elu(tk) + 1
-    a = (fq @ fk.transpose(-1, -2)) * torch.ones(50, 50).tril()
-    o32 = ((a @ tv) / a.sum(-1, keepdim=True)).numpy()
+    fq, fk = torch.nn.functional.elu(tq) + 1, torch.nn.functional.elu(tk) + 1
+    pos = torch.arange(50)
+    w = torch.einsum("bhie,bhje->bhij", fq, fk) * (pos[:, None] >= pos[None, :])
+    o32 = (torch.einsum("bhij,bhjc->bhic", w, tv) / w.sum(-1, keepdim=True)).numpy()
     err = np.abs(o32 - o64).max()
     assert err < 2e-6, err
     # and the fp32 chunked form (C = 16, ragged tail of 2) sits at the same level
