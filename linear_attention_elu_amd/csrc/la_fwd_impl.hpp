@@ -504,12 +504,13 @@ la_chunk_kernel(const FwdParams p) {
     //   dfq[I]    inter-chunk read of query row 16 I + pp: gamma^(16 I + pp + 1);
     //   dsc[D][r] score of key 16 J + 4g + r for query 16 I + pp, D = I - J:
     //             gamma^(16 D + pp - 4g - r), zero above the diagonal;
-    //   dcw[s][t] carry weight of the token in slot t of token K step s of a full
-    //             chunk: gamma^(CT - 1 - token).
+    //   dcwf[s]   carry weights of the tokens of token K step s of a full chunk,
+    //             gamma^(CT - 1 - token), as an operand (slot t: the token of
+    //             the split assignment).
     constexpr bool decay_out = decay && NEED_Q;
     float dfq[decay_out ? NB : 1];
     float dsc[decay_out ? NB : 1][4];
-    float dcw[decay ? NP : 1][8];
+    Frag<TC> dcwf[decay ? NP : 1];
     if constexpr (decay_out) {
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
@@ -527,7 +528,7 @@ la_chunk_kernel(const FwdParams p) {
 #pragma unroll
         for (int s = 0; s < NP; ++s)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) dcw[s][t] = slot_token(s, t) < CT ? gpow(CT - 1 - slot_token(s, t)) : 0.0f;
+            for (int t = 0; t < 8; ++t) dcwf[s].set(t, slot_token(s, t) < CT ? gpow(CT - 1 - slot_token(s, t)) : 0.0f);
     }
     const float g_chunk = decay ? gpow(CT) : 1.0f;  // gamma^R for a full chunk
 
@@ -772,8 +773,9 @@ la_chunk_kernel(const FwdParams p) {
         store(-1, outv, den);
 
         // ---- state carry: S(cb) += phi(K_c)^T V_c(cb), z += phi(K_c)^T 1 ----
-        // (decay: S = gamma^R S + sum_j gamma^(R - 1 - tau_j) phi(k_j) v_j^T, the
-        // weights applied to the phi(K) operand)
+        // (decay: S = gamma^R S + sum_j gamma^(R - 1 - tau_j) phi(k_j) v_j^T, z
+        // likewise: token j is the contraction index, so its weight scales the
+        // 16-column V^T operand, and it replaces the all-ones operand of z)
         if constexpr (decay) {
             if (NEED_K && has_cols) {
                 const float gR = crows == CT ? g_chunk : gpow(crows);
@@ -801,20 +803,18 @@ la_chunk_kernel(const FwdParams p) {
                         fw_lo.set(t, x - fw.get(t));
                     }
                 }
-                float cw[decay ? 8 : 1];  // carry weights of this step's tokens
-                if constexpr (decay) {
+                if constexpr (decay) {  // carry weights of this step's tokens
+                    if (crows == CT) {
+                        fw = dcwf[s];
+                    } else {
 #pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        cw[t] = crows == CT ? dcw[s][t]
-                                            : (slot_token(s, t) < crows ? gpow(crows - 1 - slot_token(s, t)) : 0.0f);
+                        for (int t = 0; t < 8; ++t)
+                            fw.set(t, slot_token(s, t) < crows ? gpow(crows - 1 - slot_token(s, t)) : 0.0f);
+                    }
                 }
 #pragma unroll
                 for (int E = 0; E < NE; ++E) {
                     lds_frag_tr(fkt[E], sk, T::LQ, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * E, pp);
-                    if constexpr (decay) {
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) fkt[E].set(t, fkt[E].get(t) * cw[t]);
-                    }
                     accZ[E] = mma(fkt[E], fw, accZ[E]);
                     if (weighted && sizeof(TC) == 2) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
                 }
@@ -824,6 +824,10 @@ la_chunk_kernel(const FwdParams p) {
                     if (col_ok(cs)) {
                         Frag<TC> fv;
                         lds_frag_tr(fv, sv, T::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cb, pp);
+                        if constexpr (decay) {
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) fv.set(t, fv.get(t) * fw.get(t));
+                        }
 #pragma unroll
                         for (int E = 0; E < NE; ++E) accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
                     }
