@@ -32,11 +32,25 @@ namespace {
 
 constexpr int kPrfThreads = 256;        // four waves
 constexpr int kPrfTokensPerBlock = 64;  // 16 tokens per wave and step
-constexpr int kPrfSteps = 4;            // token blocks per workgroup (W staged once)
+constexpr int kPrfSteps = 8;            // token blocks per workgroup (W staged once)
 
 // Rows of W (or of W^T) in LDS, padded by 16 bytes against bank conflicts of
 // the 16-byte fragment reads (lanes p = 0..15 read rows p at one column).
 template <typename TC, int D> constexpr int prf_ld() { return D + 16 / (int)sizeof(TC); }
+
+// W [M][DK] of one head into LDS with 16-byte copies, as rows of length LD
+// (TRANS: as W^T, row e holding w_{0..M-1, e}, with element copies).
+template <typename TC, int DK, int M, int LD, bool TRANS>
+__device__ __forceinline__ void stage_w(TC *sw, const TC *Wh, int tid) {
+    if constexpr (TRANS) {
+        for (int i = tid; i < M * DK; i += kPrfThreads) sw[(i % DK) * LD + i / DK] = Wh[i];
+    } else {
+        constexpr int VR = DK * (int)sizeof(TC) / 16;  // 16-byte vectors per row
+        for (int i = tid; i < M * VR; i += kPrfThreads)
+            *reinterpret_cast<uint4 *>(sw + (i / VR) * LD + (i % VR) * (16 / (int)sizeof(TC))) =
+                *reinterpret_cast<const uint4 *>(Wh + (long)i * (16 / (int)sizeof(TC)));
+    }
+}
 
 // Eight consecutive elements of a global row as an operand fragment (straight
 // K assignment: slot t of lane group g is K index 8g + t of the step).
@@ -58,11 +72,25 @@ template <typename TS> __device__ __forceinline__ void store4_to(TS *out, const 
     else *reinterpret_cast<f32x4 *>(out) = a;
 }
 
+// Four consecutive elements of a row as floats.
+template <typename TC> __device__ __forceinline__ f32x4 load4(const TC *p) {
+    if constexpr (sizeof(TC) == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u)};
+    } else {
+        return *reinterpret_cast<const f32x4 *>(p);
+    }
+}
+
 // phi(x)^T tiles: for a block of 16 tokens per wave and every feature tile F,
 // acc = W[16F.., :] x^T, so lane (g, p) ends with features 16F + 4g + r of
 // token p -- four consecutive features of one token, stored as one vector.
 // ||x||^2 comes from the same x fragments (each lane holds eight elements of
-// token p per K step; the four lane groups hold the rest).
+// token p per K step; the four lane groups hold the rest).  Each wave walks
+// kPrfSteps blocks 64 tokens apart with two register sets: the rows of block
+// i + 1 are in flight while block i is computed, and those of block 0 are
+// issued before W is staged.
 template <typename TC, typename TO, int DK, int M>
 __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
                                                              TO *__restrict__ out, int N, int H) {
@@ -71,30 +99,37 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
     __shared__ __attribute__((aligned(16))) TC sw[M * LW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, pp = lane & 15;
     const long bh = blockIdx.x;
-    const TC *Wh = W + (bh % H) * (long)M * DK;
-    for (int i = tid; i < M * DK; i += kPrfThreads) sw[(i / DK) * LW + i % DK] = Wh[i];
+    const int first = blockIdx.y * (kPrfSteps * kPrfTokensPerBlock) + 16 * wave;  // this wave's block 0
+    const TC *xb = x + bh * (long)N * DK;
+    Frag<TC> fx[2][NS];
+    auto load = [&](Frag<TC>(&f)[NS], int step) {
+        const int t = min(first + kPrfTokensPerBlock * step + pp, N - 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) frag_global8(f[s], xb + (long)t * DK + 32 * s + 8 * g);
+    };
+    load(fx[0], 0);
+    stage_w<TC, DK, M, LW, false>(sw, W + (bh % H) * (long)M * DK, tid);
     __syncthreads();
     const float scale = __builtin_amdgcn_rsqf((float)M);
+#pragma unroll
     for (int step = 0; step < kPrfSteps; ++step) {
-        const int t0 = (blockIdx.y * kPrfSteps + step) * kPrfTokensPerBlock + 16 * wave;
+        const int t0 = first + kPrfTokensPerBlock * step;
         if (t0 >= N) break;  // uniform per wave; no barrier follows
-        const int t = min(t0 + pp, N - 1);
-        const TC *xr = x + (bh * N + t) * (long)DK;
+        if (step + 1 < kPrfSteps && t0 + kPrfTokensPerBlock < N) load(fx[(step + 1) & 1], step + 1);
+        const Frag<TC>(&cx)[NS] = fx[step & 1];
         f32x4 acc[NF];
 #pragma unroll
         for (int F = 0; F < NF; ++F) acc[F] = f32x4{0.f, 0.f, 0.f, 0.f};
         float nx = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            Frag<TC> fx;
-            frag_global8(fx, xr + 32 * s + 8 * g);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) nx += fx.get(u) * fx.get(u);
+            for (int u = 0; u < 8; ++u) nx += cx[s].get(u) * cx[s].get(u);
 #pragma unroll
             for (int F = 0; F < NF; ++F) {
                 Frag<TC> fw;
                 lds_frag_straight(fw, sw + (16 * F + pp) * LW + 32 * s, g);
-                acc[F] = mma(fw, fx, acc[F]);
+                acc[F] = mma(fw, cx[s], acc[F]);
             }
         }
         nx = sum_over_groups(nx);
@@ -118,7 +153,8 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
 // significant bits (W is exact in its storage type).  That precision is
 // needed: phi(x) spans many orders of magnitude across features, so an error
 // of dphi that is small against its row but large against a small entry is
-// multiplied by a large phi_r(x).
+// multiplied by a large phi_r(x).  The token blocks are pipelined as in
+// la_prf_kernel (phi, dphi and the x elements of the epilogue in flight).
 template <typename TC, int DK, int M>
 __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
                                                                  const float *__restrict__ phi_x,
@@ -130,27 +166,40 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
     __shared__ __attribute__((aligned(16))) TC swt[DK * LT];  // W^T: row e holds w_{0..m-1, e}
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, pp = lane & 15;
     const long bh = blockIdx.x;
-    const TC *Wh = W + (bh % H) * (long)M * DK;
-    for (int i = tid; i < M * DK; i += kPrfThreads) swt[(i % DK) * LT + i / DK] = Wh[i];
+    const int first = blockIdx.y * (kPrfSteps * kPrfTokensPerBlock) + 16 * wave;
+    struct Regs {
+        Frag<float> ff[NS], fd[NS];
+        f32x4 xv[NE];
+    } rg[2];
+    auto load = [&](Regs &r, int step) {
+        const long row = bh * N + min(first + kPrfTokensPerBlock * step + pp, N - 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            frag_global8(r.ff[s], phi_x + row * M + 32 * s + 8 * g);
+            frag_global8(r.fd[s], dphi_x + row * M + 32 * s + 8 * g);
+        }
+#pragma unroll
+        for (int E = 0; E < NE; ++E) r.xv[E] = load4(x + row * DK + 16 * E + 4 * g);
+    };
+    load(rg[0], 0);
+    stage_w<TC, DK, M, LT, true>(swt, W + (bh % H) * (long)M * DK, tid);
     __syncthreads();
+#pragma unroll
     for (int step = 0; step < kPrfSteps; ++step) {
-        const int t0 = (blockIdx.y * kPrfSteps + step) * kPrfTokensPerBlock + 16 * wave;
+        const int t0 = first + kPrfTokensPerBlock * step;
         if (t0 >= N) break;  // uniform per wave; no barrier follows
-        const int t = min(t0 + pp, N - 1);
-        const long row = bh * N + t;
+        if (step + 1 < kPrfSteps && t0 + kPrfTokensPerBlock < N) load(rg[(step + 1) & 1], step + 1);
+        const Regs &cr = rg[step & 1];
         f32x4 acc[NE];
 #pragma unroll
         for (int E = 0; E < NE; ++E) acc[E] = f32x4{0.f, 0.f, 0.f, 0.f};
         float su = 0.f;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            Frag<float> ff, fd;
             Frag<TC> fu, fu_lo;
-            frag_global8(ff, phi_x + row * M + 32 * s + 8 * g);
-            frag_global8(fd, dphi_x + row * M + 32 * s + 8 * g);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float val = ff.get(u) * fd.get(u);
+                const float val = cr.ff[s].get(u) * cr.fd[s].get(u);
                 su += val;
                 fu.set(u, val);
                 if constexpr (LO) fu_lo.set(u, val - fu.get(u));
@@ -165,15 +214,9 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
         }
         su = sum_over_groups(su);
         if (t0 + pp < N) {
-            const TC *xr = x + row * DK;
-            TC *dr = dx + row * DK;
+            TC *dr = dx + (bh * N + t0 + pp) * DK;
 #pragma unroll
-            for (int E = 0; E < NE; ++E) {
-                f32x4 d;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) d[r] = acc[E][r] - static_cast<float>(xr[16 * E + 4 * g + r]) * su;
-                store4_to(dr + 16 * E + 4 * g, d);
-            }
+            for (int E = 0; E < NE; ++E) store4_to(dr + 16 * E + 4 * g, acc[E] - cr.xv[E] * su);
         }
     }
 }
