@@ -256,11 +256,14 @@ la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const vo
  * The causal forward, the non-causal forward, the causal backward and the
  * decode step with a feature map (la_feature_map above).  Arguments, layouts
  * and errors are those of the plain entry points, plus fm, W and m; the
- * workspace queries take them and the input type too (the random map keeps
- * phi(q), phi(k) -- and in the backward dphi(q), dphi(k) -- in the workspace
- * as [B][H][N][m] in the input type).  Random features are computed on the
- * matrix cores; the chunked kernels then run with the identity map over m
- * features, and the backward carries dphi back through the map:
+ * workspace queries take them and the input type too.  Random features are
+ * computed on the matrix cores.  The forwards with bf16 inputs, m = d_k = 64,
+ * d_v <= 64 and C = 64 (every non-causal call of that shape) form them in the
+ * chunked kernels as q and k are loaded, so the workspace is that of the
+ * plain forward; other shapes first write phi(q), phi(k) to the workspace as
+ * [B][H][N][m] in the input type and run the chunked kernels with the
+ * identity map over m features.  The backward keeps phi(q), phi(k), dphi(q),
+ * dphi(k) in the workspace in fp32 and carries dphi back through the map:
  * dx = sum_r dphi_r phi_r(x) (w_r - x).  An unknown fm, or m or d_k outside
  * {32, 64, 128} with LA_PHI_PRF, returns LA_ERR_UNSUPPORTED; a NULL W with
  * LA_PHI_PRF returns LA_ERR_NULL_PTR.

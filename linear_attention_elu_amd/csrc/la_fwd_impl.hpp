@@ -101,6 +101,7 @@ struct FwdParams {
     int H;                  // heads (bh % H is the head of workgroup column bh)
     int sum_P;              // MODE_APPLY: the total state is the sum of slots 0 .. sum_P - 1 (>= 1)
     int phi_id;             // feature map: 0 = elu + 1, 1 = identity (q and k are already features)
+    const void *W;          // PRF instantiations: random directions [H][DK][DK] in the input type
 };
 
 // LDS layout for one chunk of CT tokens held as TC; only the tiles a mode
@@ -133,9 +134,11 @@ template <int DK, int DV, typename TC, int CT, int MODE, bool DECAY = false> str
 // them).  A split workgroup puts two waves on every SIMD; its causal chunk
 // loop needs the registers of one workgroup per CU, its aggregate and
 // read-out passes fit two.  Four-wave workgroups get all registers.
-template <int DK, int DV, typename TI, int CT, int MODE, bool DECAY> constexpr int fwd_waves_per_eu() {
+// (The read-out with random features keeps the directions in its staging
+// waves' registers as well, and gets the registers of two waves per SIMD.)
+template <int DK, int DV, typename TI, int CT, int MODE, bool DECAY, bool PRF = false> constexpr int fwd_waves_per_eu() {
     return fwd_split<DK, DV, TI, MODE, DECAY>()
-               ? ((MODE == MODE_CAUSAL || fwd_wide_agg<DK, DV, TI, MODE, DECAY>()) ? 2 : 4)
+               ? ((MODE == MODE_CAUSAL || fwd_wide_agg<DK, DV, TI, MODE, DECAY>() || (PRF && MODE == MODE_APPLY)) ? 2 : 4)
                : 1;
 }
 
@@ -152,10 +155,13 @@ template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
 
 // OBF: the output o is bf16 (else fp32).  DECAY (MODE_CAUSAL and MODE_AGG):
 // the per-head decay of p.gamma, any value in [0, 1]; a separate
-// instantiation, so that the plain kernels keep their registers.
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false>
+// instantiation, so that the plain kernels keep their registers.  PRF: the
+// staging waves apply Performer's positive random features with as many
+// directions as input features (p.W, m = DK) instead of elu + 1 (split bf16
+// layout at CT = 64; see the staging code).
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false, bool PRF = false>
 __global__ void __launch_bounds__((fwd_threads<DK, DV, TI, MODE, DECAY>()))
-__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE, DECAY>())))
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE, DECAY, PRF>())))
 la_chunk_kernel(const FwdParams p) {
     using TC = TI;  // matrix operands keep the input precision
     using T = FwdTiles<DK, DV, TC, CT, MODE, DECAY>;
@@ -188,6 +194,8 @@ la_chunk_kernel(const FwdParams p) {
     constexpr bool WEIGHTED = MODE == MODE_AGGW;
     constexpr bool NEED_K = MODE != MODE_APPLY;
     constexpr int NKS = WEIGHTED ? NLQ : 1;  // per-vector phi(k) factors
+    static_assert(!PRF || (SPLIT && CT == 64 && NLQ == DK / 32 && !DECAY && !WEIGHTED),
+                  "random features in the staging waves: split bf16 layout, 64-token chunks");
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
     using S0t = std::integral_constant<int, 0>;
@@ -243,6 +251,25 @@ la_chunk_kernel(const FwdParams p) {
         const unsigned gv0 = (unsigned)(rv0 * DV + cv0) * sizeof(TI);
         const int lq0 = (rq0 * T::LQ + cq0) * (int)sizeof(TC);
         const int lv0 = (rv0 * T::LV + cv0) * (int)sizeof(TC);
+        // PRF: staging wave w loads q, k rows 16 w + p of the chunk in the
+        // operand layout of the projection: lane (g, p) holds elements
+        // 32 i + 8 g .. + 7 of its row in vector i (NLQ = DK / 32 vectors).
+        const int prow = 16 * wave + pp;
+        const unsigned gp0 = (unsigned)(prow * DK + 8 * g) * sizeof(TI);
+        // PRF: the directions of this head as A operands, held by the staging
+        // waves for the whole segment: wf[F][i] is rows 16 F + p, columns
+        // 32 i + 8 g .. + 7 of W (features x input elements).
+        Frag<TC> wf[PRF ? DK / 16 : 1][PRF ? NLQ : 1];
+        if constexpr (PRF) {
+            if (stager) {
+                const TC *Wh = static_cast<const TC *>(p.W) + (bh % p.H) * (long)(DK * DK);
+#pragma unroll
+                for (int F = 0; F < DK / 16; ++F)
+#pragma unroll
+                    for (int i = 0; i < NLQ; ++i)
+                        lds_frag_straight(wf[F][i], Wh + (16 * F + pp) * DK + 32 * i, g);
+            }
+        }
         // Vectors past the chunk exist only when CT * VQ is not a multiple of
         // the role size; they re-read the chunk's last row and are not staged.
         auto q_on = [&](int i) { return (CT * VQ) % kRoleThreads == 0 || rq0 + i * RSQ < CT; };
@@ -273,6 +300,7 @@ la_chunk_kernel(const FwdParams p) {
                 const char *kc = ks + (long)r0 * DK * (long)sizeof(TI);
                 const char *vc = vs + (long)r0 * DV * (long)sizeof(TI);
                 auto offq = [&](int i) {
+                    if constexpr (PRF) return gp0 + (unsigned)(32 * i * sizeof(TI));
                     return (CT * VQ) % kRoleThreads != 0 && i == NLQ - 1
                                ? (unsigned)((min(rq0 + i * RSQ, CT - 1) * DK + cq0) * sizeof(TI))
                                : gq0 + (unsigned)(i * RSQ * DK * sizeof(TI));
@@ -293,19 +321,18 @@ la_chunk_kernel(const FwdParams p) {
                     for (int i = 0; i < NLV; ++i) rv[S][i] = load_stream16(vc + offv(i));
                 }
             } else {
+                // (PRF: row prow of the chunk, elements 32 i + 8 g .. + 7)
+                auto qrow = [&](int i) -> long { return PRF ? min(r0 + prow, last) : min(r0 + rq0 + i * RSQ, last); };
+                auto qcol = [&](int i) { return PRF ? 32 * i + 8 * g : cq0; };
                 if (NEED_Q) {
 #pragma unroll
-                    for (int i = 0; i < NLQ; ++i) {
-                        const long row = min(r0 + rq0 + i * RSQ, last);
-                        rq[S][i] = load_stream16(qs + (row * DK + cq0) * (long)sizeof(TI));
-                    }
+                    for (int i = 0; i < NLQ; ++i)
+                        rq[S][i] = load_stream16(qs + (qrow(i) * DK + qcol(i)) * (long)sizeof(TI));
                 }
                 if (NEED_K) {
 #pragma unroll
-                    for (int i = 0; i < NLQ; ++i) {
-                        const long row = min(r0 + rq0 + i * RSQ, last);
-                        rk[S][i] = load_stream16(ks + (row * DK + cq0) * (long)sizeof(TI));
-                    }
+                    for (int i = 0; i < NLQ; ++i)
+                        rk[S][i] = load_stream16(ks + (qrow(i) * DK + qcol(i)) * (long)sizeof(TI));
 #pragma unroll
                     for (int i = 0; i < NLV; ++i) {
                         const long row = min(r0 + rv0 + i * RSV, last);
@@ -336,6 +363,39 @@ la_chunk_kernel(const FwdParams p) {
                                   __float_as_uint(w.get(3)));
             }
         };
+        // Random features of this wave's 16 rows (PRF): phi(x)^T tiles
+        // W[16F.., :] x^T on the matrix cores, so that lane (g, p) holds
+        // features 16 F + 4 g + r of row prow, written to the tile as four
+        // consecutive elements; |x|^2 from the same fragments (the four lane
+        // groups hold a row's elements between them).  A row past the chunk
+        // is written as zeros.
+        auto project = [&](const auto &x, char *tile, bool live) LA_INLINE {
+            if constexpr (PRF) {
+            constexpr int NF = DK / 16;
+            f32x4 acc[NF];
+#pragma unroll
+            for (int F = 0; F < NF; ++F) acc[F] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float nx = 0.f;
+#pragma unroll
+            for (int i = 0; i < NLQ; ++i) {
+                Frag<TC> fx;
+                if constexpr (sizeof(TC) == 2) fx.v = __builtin_bit_cast(bf16x8, x[i]);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) nx += fx.get(t) * fx.get(t);
+#pragma unroll
+                for (int F = 0; F < NF; ++F) acc[F] = mma(wf[F][i], fx, acc[F]);
+            }
+            nx = sum_over_groups(nx);
+            const float scale = __builtin_amdgcn_rsqf((float)DK);
+#pragma unroll
+            for (int F = 0; F < NF; ++F) {
+                f32x4 f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f[r] = live ? __expf(acc[F][r] - 0.5f * nx) * scale : 0.f;
+                *reinterpret_cast<uint2 *>(tile + (prow * T::LQ + 16 * F + 4 * g) * (int)sizeof(TC)) = pack_bf16x4(f);
+            }
+            }
+        };
         // Write set S into LDS buffer b.  FULL: all CT rows valid; otherwise
         // rows at or beyond nrows are written as zeros (they add nothing).
         auto stage = [&](auto set_tag, auto full_tag, int b, int nrows) LA_INLINE {
@@ -344,7 +404,9 @@ la_chunk_kernel(const FwdParams p) {
             char *buf = smem + b * T::BUF;
             if (weighted && sid < T::ROWS) reinterpret_cast<float *>(buf + T::OFF_W)[sid] = rw[S];
             auto keep = [&](int row) { return FULL || row < nrows; };
-            if (NEED_Q) {
+            if constexpr (PRF && NEED_Q) project(rq[S], buf + T::OFF_Q, keep(prow));
+            if constexpr (PRF && NEED_K) project(rk[S], buf + T::OFF_K, keep(prow));
+            if (NEED_Q && !PRF) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
                     if (q_on(i)) {
@@ -357,7 +419,7 @@ la_chunk_kernel(const FwdParams p) {
             if (NEED_K) {
 #pragma unroll
                 for (int i = 0; i < NLQ; ++i) {
-                    if (q_on(i)) {
+                    if (q_on(i) && !PRF) {
                         uint4 out = phi16(rk[S][i], kscaled ? rks[S][WEIGHTED ? i : 0] : 1.0f);
                         if (!keep(rq0 + i * RSQ)) out = make_uint4(0u, 0u, 0u, 0u);
                         *reinterpret_cast<uint4 *>(buf + T::OFF_K + lq0 + i * RSQ * T::LQ * (int)sizeof(TC)) = out;

@@ -11,10 +11,10 @@
 namespace la {
 
 // Resident workgroups of one instantiation of the chunk kernel (cached).
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool DECAY = false>
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool DECAY = false, bool PRF = false>
 long chunk_resident() {
     static OccCache cache;
-    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY>),
+    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY, PRF>),
                                cache, fwd_threads<DK, DV, TI, MODE, DECAY>());
 }
 
@@ -24,17 +24,18 @@ long chunk_resident() {
 // apiece), against 26.9 us with a separate total pass.
 constexpr int kNonCausalAggSegments = 4;
 
-// DECAY: the causal form with a per-head decay (d.gamma non-null).  CT: the
-// chunk of the causal and read-out kernels; CTA: that of the aggregate pass.
-template <int DK, int DV, typename TI, int CT, int CTA, bool OBF, bool DECAY>
+// DECAY: the causal form with a per-head decay (d.gamma non-null).  PRF: the
+// random-feature map in the staging waves (d.phi_id 2, d.W).  CT: the chunk
+// of the causal and read-out kernels; CTA: that of the aggregate pass.
+template <int DK, int DV, typename TI, int CT, int CTA, bool OBF, bool DECAY, bool PRF = false>
 hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     const long BH = (long)d.B * d.H;
-    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CTA, false, DECAY>;
-    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>
-                              : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF>;
+    auto agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, CTA, false, DECAY, PRF>;
+    auto main_kernel = causal ? &la_chunk_kernel<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY, PRF>
+                              : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
-    long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY>();
+    long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY, PRF>();
     // A workspace holding at most d.ws_states segment states (a fixed scratch):
     // fewer segments per (b, h), down to one, which stores no state at all.
     if (causal && d.ws_states > 0) {
@@ -42,8 +43,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
         const long cap = per_bh >= 1 ? per_bh * BH : BH;
         if (cap < target_agg) target_agg = cap;
     }
-    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY>()
-                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF>();
+    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY, PRF>()
+                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>();
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
     const long want_main = (target_main + BH - 1) / BH;
@@ -59,6 +60,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     p.N = d.N;
     p.state_P = Pf;
     p.phi_id = d.phi_id;
+    p.W = d.W;
+    p.H = d.H;
     hipError_t err;
 
     if (causal) {
@@ -132,6 +135,16 @@ template <int DK, int DV, typename TI>
 hipError_t run_fwd_t(const FwdDesc &d, bool causal) {
     const bool obf = d.out_bf16 != 0;
     const bool dec = causal && d.gamma != nullptr;
+    if (d.phi_id == kPhiPrfFused) {
+        // random features in the staging waves: the split bf16 layout at
+        // 64-token chunks, as many directions as input features
+        if constexpr (prf_fused_ok<DK, DV, TI>()) {
+            if (!dec && d.C == 64)
+                return obf ? run_fwd_ct<DK, DV, TI, 64, 64, true, false, true>(d, causal)
+                           : run_fwd_ct<DK, DV, TI, 64, 64, false, false, true>(d, causal);
+        }
+        return hipErrorInvalidValue;
+    }
     auto pick = [&](auto ct, auto cta) {
         constexpr int CT = decltype(ct)::value, CTA = decltype(cta)::value;
         if (dec) return obf ? run_fwd_ct<DK, DV, TI, CT, CTA, true, true>(d, causal)

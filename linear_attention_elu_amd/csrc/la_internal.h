@@ -23,8 +23,17 @@ struct FwdDesc {
     hipStream_t stream;
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
     long ws_states;      // causal only: if > 0, at most this many segment states fit the workspace
-    int phi_id;          // feature map: 0 = elu + 1, 1 = identity (q, k are already features)
+    int phi_id;          // feature map: 0 = elu + 1, 1 = identity (q, k are already features),
+                         // kPhiPrfFused = random features applied in the staging waves (W)
+    const void *W;       // kPhiPrfFused: directions [H][DK][DK] in the input type
 };
+
+// phi_id of the forward with the random-feature map computed in the chunk
+// kernels' staging waves (m = d_k; prf_fused_ok shapes, 64-token chunks).
+constexpr int kPhiPrfFused = 2;
+template <int DK, int DV, typename TI> constexpr bool prf_fused_ok() {
+    return sizeof(TI) == 2 && DK == 64 && DV <= 64;
+}
 
 struct DecodeDesc {
     float *S, *z;

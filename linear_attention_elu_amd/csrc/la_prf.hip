@@ -349,6 +349,14 @@ la_status check_fm(int fm, const void *W, int m, int d_k, int *mf) {
 
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
+// The forward applies the random features inside the chunk kernels' staging
+// waves (no feature tensors in HBM) for bf16 inputs with m = d_k = 64,
+// d_v <= 64 and 64-token chunks (the shapes of la::prf_fused_ok); other shapes
+// project q and k in la_prf_kernel first.
+bool prf_fused(int in, int d_k, int m, int d_v, int C) {
+    return in == LA_BF16 && d_k == 64 && m == 64 && d_v <= 64 && C == 64;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +368,7 @@ size_t la_fwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, i
     const size_t inner = la::fwd_ws_bytes(B, H, N, mf, d_v, C, true);
     if (fm != LA_PHI_PRF) return inner;
     if (B < 1 || H < 1 || N < 1 || !la::dim_ok(d_v) || !la::chunk_ok(C) || !la::dtype_ok(in)) return 0;
+    if (prf_fused(in, d_k, m, d_v, C)) return inner;
     return fm_layout(false, B, H, N, m, d_v, in, inner).total;
 }
 
@@ -370,6 +379,7 @@ size_t la_fwd_noncausal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v
     const size_t inner = la::fwd_ws_bytes(B, H, N, mf, d_v, la::kNonCausalChunk, false);
     if (fm != LA_PHI_PRF) return inner;
     if (inner == 0 || !la::dtype_ok(in)) return 0;
+    if (prf_fused(in, d_k, m, d_v, la::kNonCausalChunk)) return inner;
     return fm_layout(false, B, H, N, m, d_v, in, inner).total;
 }
 
@@ -398,7 +408,10 @@ la_status la_fwd_causal_fm(const void *q, const void *k, const void *v, void *o,
     if (fm == LA_PHI_ELU1) return la_fwd_causal(q, k, v, o, den, B, H, N, d_k, d_v, C, in, out, ws, ws_bytes, stream);
     la::FwdDesc d{q, k, v, o, den, nullptr, nullptr, nullptr, nullptr, B, H, N, mf, d_v, C,
                   in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream, nullptr, 0, 1};
-    if (fm == LA_PHI_PRF) {
+    if (fm == LA_PHI_PRF && prf_fused(in, d_k, m, d_v, C)) {
+        d.phi_id = la::kPhiPrfFused;
+        d.W = W;
+    } else if (fm == LA_PHI_PRF) {
         const FmLayout l = fm_layout(false, B, H, N, m, d_v, in, 0);
         const long BH = (long)B * H;
         hipError_t e = la::launch_prf(in == LA_BF16, la::PRF_PHI, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k,
@@ -430,7 +443,10 @@ la_status la_fwd_noncausal_fm(const void *q, const void *k, const void *v, void 
     if (fm == LA_PHI_ELU1) return la_fwd_noncausal(q, k, v, o, B, H, N, d_k, d_v, in, out, ws, ws_bytes, stream);
     la::FwdDesc d{q, k, v, o, nullptr, nullptr, nullptr, nullptr, nullptr, B, H, N, mf, d_v, la::kNonCausalChunk,
                   in == LA_BF16, out == LA_BF16, static_cast<float *>(ws), stream, nullptr, 0, 1};
-    if (fm == LA_PHI_PRF) {
+    if (fm == LA_PHI_PRF && prf_fused(in, d_k, m, d_v, la::kNonCausalChunk)) {
+        d.phi_id = la::kPhiPrfFused;
+        d.W = W;
+    } else if (fm == LA_PHI_PRF) {
         const FmLayout l = fm_layout(false, B, H, N, m, d_v, in, 0);
         const long BH = (long)B * H;
         hipError_t e = la::launch_prf(in == LA_BF16, la::PRF_PHI, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k,
