@@ -195,9 +195,10 @@ def bench_fwd_prf(steps, warmup, dev, B=8, H=8, N=65536, d=64, m=64, C=64, seed=
     """The headline shape with Performer's positive random features (m = 64
     directions per head, orthogonal blocks): q, k ~ N(0, d^-1/2), as the map is
     used.  Algorithmic bytes are the call's inputs and output (q, k, v read, o
-    written: 512 B per token-head; W is 8 KB per head); the features pass through
-    the workspace (2 x m x 2 B written and read per token-head), which the
-    fraction does not count as useful bytes."""
+    written: 512 B per token-head; W is 8 KB per head).  At this shape the
+    features are formed in the chunk kernels as q and k are loaded; other shapes
+    pass them through the workspace (2 x m x 2 B written and read per
+    token-head), which the fraction would not count as useful bytes."""
     import torch
 
     import linear_attention_elu_amd as la
