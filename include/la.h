@@ -257,8 +257,8 @@ la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const vo
  * decode step with a feature map (la_feature_map above).  Arguments, layouts
  * and errors are those of the plain entry points, plus fm, W and m; the
  * workspace queries take them and the input type too.  Random features are
- * computed on the matrix cores.  The forwards with bf16 inputs, m = d_k = 64,
- * d_v <= 64 and C = 64 (every non-causal call of that shape) form them in the
+ * computed on the matrix cores.  The forwards with bf16 inputs, m = d_k in
+ * {32, 64}, d_v <= 64 and C = 64 (every non-causal call of such a shape) form them in the
  * chunked kernels as q and k are loaded, so the workspace is that of the
  * plain forward; other shapes first write phi(q), phi(k) to the workspace as
  * [B][H][N][m] in the input type and run the chunked kernels with the

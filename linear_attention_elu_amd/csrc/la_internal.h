@@ -32,7 +32,7 @@ struct FwdDesc {
 // kernels' staging waves (m = d_k; prf_fused_ok shapes, 64-token chunks).
 constexpr int kPhiPrfFused = 2;
 template <int DK, int DV, typename TI> constexpr bool prf_fused_ok() {
-    return sizeof(TI) == 2 && DK == 64 && DV <= 64;
+    return sizeof(TI) == 2 && (DK == 32 || DK == 64) && DV <= 64;
 }
 
 struct DecodeDesc {

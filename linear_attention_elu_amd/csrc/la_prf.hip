@@ -350,11 +350,11 @@ la_status check_fm(int fm, const void *W, int m, int d_k, int *mf) {
 char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 // The forward applies the random features inside the chunk kernels' staging
-// waves (no feature tensors in HBM) for bf16 inputs with m = d_k = 64,
+// waves (no feature tensors in HBM) for bf16 inputs with m = d_k in {32, 64},
 // d_v <= 64 and 64-token chunks (the shapes of la::prf_fused_ok); other shapes
 // project q and k in la_prf_kernel first.
 bool prf_fused(int in, int d_k, int m, int d_v, int C) {
-    return in == LA_BF16 && d_k == 64 && m == 64 && d_v <= 64 && C == 64;
+    return in == LA_BF16 && (d_k == 32 || d_k == 64) && m == d_k && d_v <= 64 && C == 64;
 }
 
 }  // namespace

@@ -58,6 +58,8 @@ PRF_CASES = [  # (B, H, N, d_k, d_v, m, C)
     (1, 2, 5000, 64, 64, 64, 64),   # several segments per (batch, head)
     (2, 3, 700, 64, 32, 64, 64),    # d_v = 32 and 16 with m = d_k = 64 (the features formed in the chunk kernels)
     (1, 1, 130, 64, 16, 64, 64),
+    (1, 2, 300, 32, 32, 32, 64),    # m = d_k = 32 in the chunk kernels
+    (2, 1, 77, 32, 64, 32, 64),
 ]
 
 
