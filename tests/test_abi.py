@@ -221,11 +221,24 @@ def test_feature_map_entry_points_reject(lib):
     bad[6] = MIS                                      # W alignment
     assert f(*bad) == 7
     bad = list(args)
-    bad[-3] = None                                    # workspace (the features need one)
+    bad[14] = bad[15] = 0                             # fp32: the features pass through the workspace
+    bad[-3] = None                                    # ... which is missing
     bad[-2] = 0
     assert f(*bad) == 5
-    assert la.la_fwd_causal_fm_workspace_bytes(1, 1, 64, 64, 64, 64, "prf", 64, __import__("torch").bfloat16) > 0
     assert lib.la_fwd_causal_fm_workspace_bytes(1, 1, 64, 64, 64, 64, 9, 64, 1) == 0
+    # bf16 with m = d_k in {32, 64}, d_v <= 64, C = 64: the features are formed in
+    # the chunk kernels, so the workspace is the plain forward's; other shapes add
+    # phi(q), phi(k) as [B][H][N][m] in the input type
+    torch = __import__("torch")
+    for B, H, N, dk, dv in ((2, 3, 5000, 64, 64), (1, 2, 300, 32, 16), (8, 8, 65536, 64, 32)):
+        plain = lib.la_fwd_causal_workspace_bytes(B, H, N, dk, dv, 64)
+        assert la.la_fwd_causal_fm_workspace_bytes(B, H, N, dk, dv, 64, "prf", dk, torch.bfloat16) == plain
+        assert lib.la_fwd_noncausal_fm_workspace_bytes(B, H, N, dk, dv, 2, dk, 1) == \
+            lib.la_fwd_noncausal_workspace_bytes(B, H, N, dk, dv)
+        for C, m, dt in ((32, dk, 1), (64, dk, 0), (64, 2 * dk, 1)):
+            inner = lib.la_fwd_causal_workspace_bytes(B, H, N, m, dv, C)
+            got = lib.la_fwd_causal_fm_workspace_bytes(B, H, N, dk, dv, C, 2, m, dt)
+            assert got >= inner + 2 * B * H * N * m * (2 if dt == 1 else 4), (B, H, N, dk, dv, C, m, dt)
     g = lib.la_decode_step_fm
     assert g(P, P, P, P, P, P, 2, None, 64, 1, 1, 64, 64, 1, None) == 1
     assert g(P, P, P, P, P, P, 2, P, 16, 1, 1, 64, 64, 1, None) == 3
