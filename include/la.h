@@ -34,8 +34,10 @@
  *             normaliser z [B][H][d_k], per-token denominators [B][H][N],
  *             per-step decode vectors [B][H][d], per-head decays [H].
  *             Every tensor pointer must be 16-byte aligned (gamma: 4-byte).
- *   Sizes     d_k, d_v in {16, 32, 64, 128}, chosen independently; N >= 1 and
- *             need not be a multiple of C; C in {16, 32, 64}; B, H >= 1.
+ *   Sizes     d_k, d_v in {16, 32, 64, 128}, chosen independently;
+ *             1 <= N <= 2^30 (LA_ERR_BAD_SHAPE beyond; the workspace queries
+ *             return 0), N need not be a multiple of C; C in {16, 32, 64};
+ *             B, H >= 1.
  *   Dtypes    `in` is the storage type of q, k, v (and dO, dq, dk, dv);
  *             `out` that of o.  S, z and den are always fp32.  Arithmetic is
  *             fp32 accumulate; for LA_BF16 inputs the matrix products take

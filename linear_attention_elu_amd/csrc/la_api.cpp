@@ -52,13 +52,13 @@ bool aligned_or_null(const void *p) { return p == nullptr || aligned(p); }
 
 // B, H, N within what the kernels index with 32-bit grid sizes and 64-bit offsets.
 la_status check_shape(int B, int H, int N) {
-    if (B < 1 || H < 1 || N < 1) return LA_ERR_BAD_SHAPE;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN) return LA_ERR_BAD_SHAPE;
     if ((long long)B * H > 0x7fffffffLL) return LA_ERR_BAD_SHAPE;
     return LA_OK;
 }
 
 size_t fwd_ws_bytes(int B, int H, int N, int dk, int dv, int C, bool causal) {
-    if (B < 1 || H < 1 || N < 1 || !dim_ok(dk) || !dim_ok(dv) || !chunk_ok(C)) return 0;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || !dim_ok(dk) || !dim_ok(dv) || !chunk_ok(C)) return 0;
     const long BH = (long)B * H;
     int L = 0;
     const int P = plan_segments(BH, N, C, kMaxTargetWg, &L);
@@ -141,12 +141,12 @@ size_t la_fwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v) {
 }
 
 size_t la_bwd_causal_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C) {
-    if (B < 1 || H < 1 || N < 1 || !dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return 0;
+    if (B < 1 || H < 1 || N < 1 || N > la::kMaxN || !dim_ok(d_k) || !dim_ok(d_v) || !chunk_ok(C)) return 0;
     return la::bwd_workspace_bytes(B, H, N, d_k, d_v, C);
 }
 
 size_t la_bwd_noncausal_workspace_bytes(int B, int H, int N, int d_k, int d_v) {
-    if (B < 1 || H < 1 || N < 1 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+    if (B < 1 || H < 1 || N < 1 || N > la::kMaxN || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
     return la::bwd_workspace_bytes(B, H, N, d_k, d_v, kNonCausalChunk);
 }
 

@@ -69,6 +69,9 @@ struct BwdDesc {
 constexpr long kMaxTargetWg = 2048;
 int plan_segments(long BH, int N, int C, long target_wg, int *L);
 
+// Longest sequence accepted (segment bounds are int arithmetic on N + L).
+constexpr int kMaxN = 1 << 30;
+
 // Workgroups of `kernel` (`threads` per workgroup) the current device keeps resident at
 // once: occupancy per CU times the CU count, at most kMaxTargetWg.  Cached per
 // device in `cache`, which belongs to that one kernel (a function-local static

@@ -367,7 +367,7 @@ size_t la_fwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, i
     if (check_fm(fm, fm == LA_PHI_PRF ? (const void *)16 : nullptr, m, d_k, &mf) != LA_OK) return 0;
     const size_t inner = la::fwd_ws_bytes(B, H, N, mf, d_v, C, true);
     if (fm != LA_PHI_PRF) return inner;
-    if (B < 1 || H < 1 || N < 1 || !la::dim_ok(d_v) || !la::chunk_ok(C) || !la::dtype_ok(in)) return 0;
+    if (B < 1 || H < 1 || N < 1 || N > la::kMaxN || !la::dim_ok(d_v) || !la::chunk_ok(C) || !la::dtype_ok(in)) return 0;
     if (prf_fused(in, d_k, m, d_v, C)) return inner;
     return fm_layout(false, B, H, N, m, d_v, in, inner).total;
 }
@@ -387,7 +387,7 @@ size_t la_bwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, i
                                         la_dtype in) {
     int mf = 0;
     if (check_fm(fm, fm == LA_PHI_PRF ? (const void *)16 : nullptr, m, d_k, &mf) != LA_OK) return 0;
-    if (B < 1 || H < 1 || N < 1 || !la::dim_ok(mf) || !la::dim_ok(d_v) || !la::chunk_ok(C)) return 0;
+    if (B < 1 || H < 1 || N < 1 || N > la::kMaxN || !la::dim_ok(mf) || !la::dim_ok(d_v) || !la::chunk_ok(C)) return 0;
     const size_t inner = la::bwd_workspace_bytes(B, H, N, mf, d_v, C);
     if (fm != LA_PHI_PRF) return inner;
     if (!la::dtype_ok(in)) return 0;

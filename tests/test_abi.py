@@ -61,6 +61,11 @@ def test_workspace_queries(lib):
     assert la.la_fwd_causal_workspace_bytes(1, 1, 64, 48, 64, 64) == 0
     assert la.la_fwd_causal_workspace_bytes(1, 1, 64, 64, 64, 8) == 0
     assert la.la_fwd_causal_workspace_bytes(0, 1, 64, 64, 64, 64) == 0
+    # sequences up to 2^30 tokens
+    assert la.la_fwd_causal_workspace_bytes(1, 1, 1 << 30, 64, 64, 64) > 0
+    for q in (lib.la_fwd_causal_workspace_bytes, lib.la_bwd_causal_workspace_bytes):
+        assert q(1, 1, (1 << 30) + 1, 64, 64, 64) == 0
+    assert lib.la_fwd_noncausal_workspace_bytes(1, 1, (1 << 30) + 1, 64, 64) == 0
 
 
 def _causal(lib, q=P, k=P, v=P, o=P, den=None, B=1, H=1, N=64, dk=64, dv=64, C=64, tin=1, tout=1,
@@ -73,6 +78,7 @@ def test_fwd_causal_rejects(lib):
     assert _causal(lib, o=None) == 1
     assert _causal(lib, B=0) == 2
     assert _causal(lib, N=0) == 2
+    assert _causal(lib, N=(1 << 30) + 1) == 2
     assert _causal(lib, H=-3) == 2
     assert _causal(lib, dk=48) == 3
     assert _causal(lib, dv=256) == 3
