@@ -92,6 +92,19 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
         }
     };
 
+    // The normaliser's operands (z, and q, k at this lane's features) are
+    // loaded here, with the other loads of the step: issued after the state's
+    // stores they cost a second memory round trip per step.
+    float zr[NFH], qr[NFH], kr[NFH];
+#pragma unroll
+    for (int h = 0; h < NFH; ++h) {
+        const int e = min(lane + 64 * h, DK - 1);  // lanes past d_k re-read the last feature, unused
+        zr[h] = z[bh * (long)DK + e];
+        if constexpr (FM != FM_PRF) {
+            qr[h] = Store<TI>::load(q, qk0 + e);
+            kr[h] = Store<TI>::load(k, qk0 + e);
+        }
+    }
     float vv[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) vv[t] = Store<TI>::load(v, bh * (long)DV + 4 * cg + t);
@@ -126,26 +139,26 @@ la_decode_kernel(float *__restrict__ S, float *__restrict__ z, const void *__res
 #pragma unroll
         for (int c = 0; c < 4; ++c) num[c] += __shfl_xor(num[c], off, 64);
 
+    // (computed on every lane, so that the loads above have a use outside the
+    // store's branch and stay where they are issued)
     float dpart = 0.f;
 #pragma unroll
-    for (int h = 0; h < (DK + 63) / 64; ++h) {
+    for (int h = 0; h < NFH; ++h) {
         const int e = lane + 64 * h;
-        if (e < DK) {
-            float fk, fq;
-            if constexpr (FM == FM_PRF) {
-                fk = fkh[h];
-                fq = fqh[h];
-            } else if constexpr (FM == FM_ID) {
-                fk = Store<TI>::load(k, qk0 + e);
-                fq = Store<TI>::load(q, qk0 + e);
-            } else {
-                fk = phi(Store<TI>::load(k, qk0 + e));
-                fq = phi(Store<TI>::load(q, qk0 + e));
-            }
-            const float zn = gm * z[bh * (long)DK + e] + fk;
-            z[bh * (long)DK + e] = zn;
-            dpart += fq * zn;
+        float fk, fq;
+        if constexpr (FM == FM_PRF) {
+            fk = fkh[h];
+            fq = fqh[h];
+        } else if constexpr (FM == FM_ID) {
+            fk = kr[h];
+            fq = qr[h];
+        } else {
+            fk = phi(kr[h]);
+            fq = phi(qr[h]);
         }
+        const float zn = gm * zr[h] + fk;
+        dpart += e < DK ? fq * zn : 0.f;
+        if (e < DK) z[bh * (long)DK + e] = zn;
     }
 #pragma unroll
     for (int off = 1; off < 64; off *= 2) dpart += __shfl_xor(dpart, off, 64);
