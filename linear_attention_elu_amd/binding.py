@@ -324,9 +324,10 @@ def _fm_args(feature_map, W, q):
         raise ValueError(f"feature_map must be one of {sorted(_FM)}") from None
     if code != _lib.LA_PHI_PRF:
         return code, None, q.shape[-1]
-    if W is None or W.dim() != 3 or W.dtype != q.dtype or W.shape[2] != q.shape[-1]:
+    # q is [B, H, N, d_k] or, for a decode step, [B, H, d_k]: H is dim 1 in both
+    if W is None or W.dim() != 3 or W.dtype != q.dtype or W.shape[0] != q.shape[1] or W.shape[2] != q.shape[-1]:
         raise ValueError("feature_map='prf' needs W [H, m, d_k] in the dtype of q")
-    _dev(W)
+    _dev(q, W)
     return code, W, W.shape[1]
 
 
@@ -348,8 +349,8 @@ def la_fwd_causal_fm(q, k, v, feature_map="elu1", W=None, o=None, den=None, C: i
                      stream=None, want_den: bool = True):
     """Causal forward with a feature map.  Returns (o, den)."""
     B, H, N, dk, dv = _shapes(q, k, v)
-    dev = _dev(q, k, v, o, den, ws)
     code, W, m = _fm_args(feature_map, W, q)
+    dev = _dev(q, k, v, o, den, ws)
     if o is None:
         o = torch.empty((B, H, N, dv), dtype=out_dtype or q.dtype, device=dev)
     if den is None and want_den:
@@ -367,8 +368,8 @@ def la_fwd_causal_fm(q, k, v, feature_map="elu1", W=None, o=None, den=None, C: i
 def la_fwd_noncausal_fm(q, k, v, feature_map="elu1", W=None, o=None, out_dtype=None, ws=None, stream=None):
     """Non-causal forward with a feature map.  Returns o."""
     B, H, N, dk, dv = _shapes(q, k, v)
-    dev = _dev(q, k, v, o, ws)
     code, W, m = _fm_args(feature_map, W, q)
+    dev = _dev(q, k, v, o, ws)
     if o is None:
         o = torch.empty((B, H, N, dv), dtype=out_dtype or q.dtype, device=dev)
     if tuple(o.shape) != (B, H, N, dv):
@@ -385,8 +386,8 @@ def la_bwd_causal_fm(q, k, v, dO, feature_map="elu1", W=None, dq=None, dk=None, 
                      stream=None):
     """Backward of la_fwd_causal_fm.  Returns (dq, dk, dv) in the dtype of q."""
     B, H, N, d_k, d_v = _shapes(q, k, v)
-    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
     code, W, m = _fm_args(feature_map, W, q)
+    dev = _dev(q, k, v, dO, dq, dk, dv, ws)
     if tuple(dO.shape) != (B, H, N, d_v) or dO.dtype != q.dtype:
         raise ValueError("dO must be [B,H,N,d_v] in the dtype of q")
     dq = torch.empty_like(q) if dq is None else dq

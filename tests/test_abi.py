@@ -296,3 +296,25 @@ def test_binding_refuses_cpu_tensors(lib):
         la.la_fwd_causal(q, q, q)
     with pytest.raises(ValueError):
         la.la_decode_step(torch.zeros(1, 1, 16, 16), torch.zeros(1, 1, 16), q[0, :, 0], q[0, :, 0], q[0, :, 0])
+
+
+def test_binding_checks_random_feature_directions(lib):
+    """W must be [H, m, d_k] in q's dtype: the kernels index it by head, so a
+    W with fewer heads than q would be read past its end.  The shape checks come
+    before any device work (CPU tensors suffice)."""
+    import torch
+    q = torch.zeros(2, 3, 16, 32, dtype=torch.bfloat16)
+    for W in (torch.zeros(2, 32, 32, dtype=torch.bfloat16),     # 2 heads for 3
+              torch.zeros(3, 32, 16, dtype=torch.bfloat16),     # d_k 16 for 32
+              torch.zeros(3, 32, 32, dtype=torch.float32),      # dtype
+              torch.zeros(32, 32, dtype=torch.bfloat16),        # rank
+              None):
+        with pytest.raises(ValueError, match="needs W"):
+            la.la_fwd_causal_fm(q, q, q, "prf", W)
+        with pytest.raises(ValueError, match="needs W"):
+            la.la_fwd_noncausal_fm(q, q, q, "prf", W)
+        with pytest.raises(ValueError, match="needs W"):
+            la.la_bwd_causal_fm(q, q, q, q, "prf", W)
+        with pytest.raises(ValueError, match="needs W"):
+            la.la_decode_step_fm(torch.zeros(2, 3, 32, 32), torch.zeros(2, 3, 32), q[:, :, 0], q[:, :, 0],
+                                 q[:, :, 0], "prf", W)
