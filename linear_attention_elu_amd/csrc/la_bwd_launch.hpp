@@ -138,8 +138,8 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     float *suf = reinterpret_cast<float *>(ws + lay.suf);
     hipError_t err;
 
-    // The aggregate passes reuse the forward's chunk kernel at the caller's
-    // chunk size: plain for the prefix sums, weighted for the suffix sums.
+    // The prefix aggregate reuses the forward's chunk kernel at the caller's
+    // chunk size (the suffix sums come from the dq sweep).
     void (*agg_kernel)(const FwdParams) = nullptr;
     long target_agg = 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
