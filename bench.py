@@ -54,7 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="skip the sweep / non-causal / backward lines")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "decay", "prf", "copy"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "noncausal", "bwd", "decay", "prf", "decay_bwd", "prf_bwd",
+                                       "copy"], default=None,
                     help="run one leg only (for profiler runs); prints its own JSON line")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the plain copy leg")
     return ap.parse_args()
@@ -359,6 +360,58 @@ def bench_bwd(dev, steps=20, warmup=20, B=8, H=16, N=8192, d=128, C=64, seed=0):
     return res
 
 
+def bench_decay_bwd(dev, steps=20, warmup=20, B=8, H=16, N=8192, d=128, C=64, seed=0):
+    """Forward and backward with a fixed decay per head (1 - 2^-(3 + h/2)) at the
+    backward workload's shape.  Bytes as in bench_bwd (den is not stored)."""
+    import torch
+
+    import linear_attention_elu_amd as la
+    from linear_attention_elu_amd import inputs
+
+    host = inputs.attention_inputs(B, H, N, d, d, seed=seed, with_grad=True)
+    q, k, v, dO = (inputs.to_torch(host[n], torch.bfloat16, dev) for n in ("q", "k", "v", "dO"))
+    del host
+    stream = torch.cuda.current_stream(dev)
+    g = torch.tensor([1.0 - 2.0 ** -(3 + h / 2) for h in range(H)], dtype=torch.float32, device=dev)
+    o = torch.empty(B, H, N, d, dtype=torch.bfloat16, device=dev)
+    wsf = torch.empty(max(1, la.la_fwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
+    fwd_ms = time_calls(lambda: la.la_fwd_causal_decay(q, k, v, g, o=o, C=C, ws=wsf, want_den=False), steps, warmup,
+                        stream)
+    wsb = torch.empty(max(1, la.la_bwd_causal_workspace_bytes(B, H, N, d, d, C)), dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    bwd_ms = time_calls(lambda: la.la_bwd_causal_decay(q, k, v, dO, g, dq=dq, dk=dk, dv=dv, C=C, ws=wsb),
+                        steps, warmup, stream)
+    fwd_bytes, bwd_bytes = B * H * N * 4 * d * 2, B * H * N * 7 * d * 2
+    return {"workload": f"causal_decay_fwd_bwd_bf16_B{B}_H{H}_N{N}_d{d}_C{C}", "fwd_us": round(fwd_ms * 1e3, 2),
+            "fwd_hbm_frac": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_us": round(bwd_ms * 1e3, 2), "bwd_hbm_frac": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def bench_prf_bwd(dev, steps=5, warmup=3, B=8, H=8, N=65536, d=64, m=64, C=64, seed=0):
+    """Backward with Performer's random features (m = 64) at the headline shape.
+    Algorithmic bytes are the call's (q, k, v, dO read; dq, dk, dv written: 7 d x 2 B
+    per token-head); the features and their gradients pass through the workspace
+    in fp32, which the fraction does not count as useful bytes."""
+    import torch
+
+    import linear_attention_elu_amd as la
+    from linear_attention_elu_amd import inputs
+
+    host = inputs.attention_inputs(B, H, N, d, d, seed=seed, with_grad=True, qk_std=d ** -0.25)
+    q, k, v, dO = (inputs.to_torch(host[n], torch.bfloat16, dev) for n in ("q", "k", "v", "dO"))
+    del host
+    W = inputs.to_torch(inputs.random_features(H, m, d, seed=seed + 1), torch.bfloat16, dev)
+    ws = torch.empty(max(1, la.la_bwd_causal_fm_workspace_bytes(B, H, N, d, d, C, "prf", m, torch.bfloat16)),
+                     dtype=torch.uint8, device=dev)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ms = time_calls(lambda: la.la_bwd_causal_fm(q, k, v, dO, "prf", W, dq=dq, dk=dk, dv=dv, C=C, ws=ws), steps, warmup,
+                    torch.cuda.current_stream(dev))
+    by = B * H * N * 7 * d * 2
+    return {"workload": f"causal_prf_bwd_bf16_B{B}_H{H}_N{N}_d{d}_m{m}_C{C}", "us": round(ms * 1e3, 2),
+            "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workspace_bytes": ws.numel()}
+
+
 def bench_copy(dev, mib, steps=10, warmup=2):
     """A plain device copy of known size (the reference for HBM counters)."""
     import torch
@@ -433,6 +486,10 @@ def main():
             r = bench_fwd_decay(args.steps, args.warmup, dev)
         elif args.only == "prf":
             r = bench_fwd_prf(args.steps, args.warmup, dev)
+        elif args.only == "decay_bwd":
+            r = bench_decay_bwd(dev, args.steps, args.warmup)
+        elif args.only == "prf_bwd":
+            r = bench_prf_bwd(dev, args.steps, args.warmup)
         else:
             r = bench_copy(dev, args.copy_mib, args.steps, args.warmup)
         print(json.dumps({"only": args.only, **r}))
@@ -483,7 +540,8 @@ def main():
             sweep[str(2 ** e)] = bench_sweep_point(dev, 2 ** e, max(5, args.steps), 20)
         res["extra"] = {"causal_sweep_B8_H8_d64_C64": sweep, "noncausal": bench_noncausal(dev),
                         "fwd_bwd": bench_bwd(dev), "causal_decay": bench_fwd_decay(args.steps, args.warmup, dev),
-                        "causal_prf": bench_fwd_prf(args.steps, args.warmup, dev)}
+                        "causal_prf": bench_fwd_prf(args.steps, args.warmup, dev),
+                        "decay_fwd_bwd": bench_decay_bwd(dev), "causal_prf_bwd": bench_prf_bwd(dev)}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on host cores")
         res["cpu_baseline"] = cpu_baseline()

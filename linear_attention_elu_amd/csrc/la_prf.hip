@@ -222,10 +222,31 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
 }
 
 // Element-wise type conversion of n values (bf16 <-> fp32 staging of the
-// random-feature backward).
+// random-feature backward), eight per thread and step with 16-byte accesses
+// (both buffers 16-byte aligned); the last n % 8 values one by one.
 template <typename TA, typename TB>
 __global__ void __launch_bounds__(256) la_convert_kernel(const TA *__restrict__ a, TB *__restrict__ b, long n) {
-    for (long i = blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256L)
+    const long nv = n / 8;
+    for (long i = blockIdx.x * 256L + threadIdx.x; i < nv; i += (long)gridDim.x * 256L) {
+        float x[8];
+        if constexpr (sizeof(TA) == 2) {
+            const uint4 u = load_stream16(a + 8 * i);
+            unpack16(u, x, __bf16());
+        } else {
+            const uint4 u0 = load_stream16(a + 8 * i), u1 = load_stream16(a + 8 * i + 4);
+            x[0] = __uint_as_float(u0.x), x[1] = __uint_as_float(u0.y), x[2] = __uint_as_float(u0.z);
+            x[3] = __uint_as_float(u0.w), x[4] = __uint_as_float(u1.x), x[5] = __uint_as_float(u1.y);
+            x[6] = __uint_as_float(u1.z), x[7] = __uint_as_float(u1.w);
+        }
+        if constexpr (sizeof(TB) == 2) {
+            const uint2 lo = pack_bf16x4(f32x4{x[0], x[1], x[2], x[3]}), hi = pack_bf16x4(f32x4{x[4], x[5], x[6], x[7]});
+            *reinterpret_cast<uint4 *>(b + 8 * i) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            *reinterpret_cast<f32x4 *>(b + 8 * i) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4 *>(b + 8 * i + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        }
+    }
+    for (long i = 8 * nv + blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256L)
         b[i] = static_cast<TB>(static_cast<float>(a[i]));
 }
 
@@ -281,7 +302,9 @@ hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const v
 
 hipError_t launch_convert(bool to_f32, const void *a, void *b, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const long blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+    long blocks = (n / 8 + 255) / 256;  // eight values per thread
+    if (blocks < 1) blocks = 1;
+    if (blocks > 8192) blocks = 8192;
     if (to_f32)
         la_convert_kernel<__bf16, float><<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const __bf16 *>(a),
                                                                                static_cast<float *>(b), n);
