@@ -23,7 +23,8 @@
  *   - gradient as cumulative sums with linear memory: velog 3.5; blog digest
  *     "Methods" (last item);
  *   - fixed per-head decay of the state: itwiki, table of later variants,
- *     RetNet row (la_fwd_causal_decay, la_decode_step_decay);
+ *     RetNet row (la_fwd_causal_decay, la_bwd_causal_decay,
+ *     la_decode_step_decay);
  *   - choice of feature map (elu + 1, Performer's positive random features,
  *     identity): itwiki section "특징 사상 선택"; blog digest "Digest"
  *     (the *_fm entry points).
