@@ -162,8 +162,9 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     static OccCache occ_dq, occ_kv;
     const long target_dq = resident_workgroups(reinterpret_cast<const void *>(dq_kernel), occ_dq, kBwdThreads);
     const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
+    const long target_sweep = target_dq < target_kv ? target_dq : target_kv;
     int Lf = 0;
-    const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
+    const int Pf = plan_segments(BH, d.N, d.C, fine_target(BH, (target_sweep + BH - 1) / BH, target_agg), &Lf);
     auto split = [&](long target, int *mult) {
         const long want = (target + BH - 1) / BH;
         *mult = (int)((Pf + want - 1) / want);
@@ -172,7 +173,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     // One split for both sweeps: the dq sweep leaves each segment's suffix sums
     // for the dk/dv sweep's segments.
     int mult = 1;
-    const int Pc = split(target_dq < target_kv ? target_dq : target_kv, &mult);
+    const int Pc = split(target_sweep, &mult);
     const int Lc = Lf * mult;
 
     FwdParams a{};

@@ -18,6 +18,21 @@ long chunk_resident() {
                                cache, fwd_threads<DK, DV, TI, MODE, DECAY>());
 }
 
+// Workgroup target for the fine segments of an aggregate pass that feeds
+// `want` causal segments per (b, h).  The pass sums only the fine segments
+// before the last causal segment, (want - 1) * mult per (b, h), so mult fine
+// segments per causal segment are chosen to fill one round of the `resident`
+// aggregate workgroups.  At B=8, H=16, N=8192, d=128 (two causal segments
+// per (b, h)) a single fine segment each left half of the CUs idle.
+inline long fine_target(long BH, long want, long resident) {
+    long t = resident;
+    if (want > 1) {
+        const long mult = resident / ((want - 1) * BH);
+        if (mult > 1) t = mult * want * BH;
+    }
+    return t < kMaxTargetWg ? t : kMaxTargetWg;
+}
+
 // Aggregate segments per (b, h) of the non-causal form (at most).  At B=4,
 // H=8, N=4096, d=64 the forward took 29.1 us with 2, 23.2 with 4, 22.8 with 8
 // and 29.2 with 16 (each read-out workgroup sums them: d_k (d_v + 1) floats
@@ -35,7 +50,11 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
                               : &la_chunk_kernel<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>;
     // Each launch aims at one round of resident workgroups.  The aggregate
     // pass uses fine segments; a causal segment is a run of `mult` of them.
+    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY, PRF>()
+                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>();
+    const long want_main = (target_main + BH - 1) / BH;
     long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY, PRF>();
+    if (causal) target_agg = fine_target(BH, want_main, target_agg);
     // A workspace holding at most d.ws_states segment states (a fixed scratch):
     // fewer segments per (b, h), down to one, which stores no state at all.
     if (causal && d.ws_states > 0) {
@@ -43,11 +62,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
         const long cap = per_bh >= 1 ? per_bh * BH : BH;
         if (cap < target_agg) target_agg = cap;
     }
-    const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY, PRF>()
-                                    : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>();
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
-    const long want_main = (target_main + BH - 1) / BH;
     const int mult = (int)((Pf + want_main - 1) / want_main);
     const int Pm = (Pf + mult - 1) / mult;
 
