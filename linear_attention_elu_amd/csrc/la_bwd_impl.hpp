@@ -537,19 +537,26 @@ la_bwd_dq_kernel(const BwdParams p) {
             }
 #pragma unroll
             for (int s = 0; s < NTS; ++s) {
+                // weighted phi(k) as a value and its remainder (bf16), as in the
+                // aggregate that feeds the segment states
+                Frag<TC> fkl;
                 if constexpr (dec) {
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
                         const int tok = 32 * s + (t < 4 ? 4 * g + t : 16 + 4 * g + t - 4);
-                        fkt[s].set(t, tok < nrows ? fkt[s].get(t) * dcy.pow(nrows - 1 - tok) : 0.0f);
+                        const float x = tok < nrows ? fkt[s].get(t) * dcy.pow(nrows - 1 - tok) : 0.0f;
+                        fkt[s].set(t, x);
+                        if constexpr (SLO) fkl.set(t, x - fkt[s].get(t));
                     }
                 }
                 accZ = mma(fkt[s], ones, accZ);
+                if constexpr (dec && SLO) accZ = mma(fkl, ones, accZ);
 #pragma unroll
                 for (int cv = 0; cv < CV; ++cv) {
                     Frag<TC> fvt;
                     lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
                     accS[cv] = mma(fvt, fkt[s], accS[cv]);
+                    if constexpr (dec && SLO) accS[cv] = mma(fvt, fkl, accS[cv]);
                 }
             }
             refresh();

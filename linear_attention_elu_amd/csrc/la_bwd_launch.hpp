@@ -139,21 +139,23 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     hipError_t err;
 
     // The prefix aggregate reuses the forward's chunk kernel at the caller's
-    // chunk size (the suffix sums come from the dq sweep).
+    // chunk size (the suffix sums come from the dq sweep); decayed on bf16
+    // operands, in its value-plus-remainder carry variant.
+    constexpr bool XC = DECAY && sizeof(TI) == 2;
     void (*agg_kernel)(const FwdParams) = nullptr;
     long target_agg = 0;
     switch (fwd_chunk<DK, DV, TI>(d.C)) {
         case 16:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false, DECAY>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16, false, DECAY>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16, false, DECAY, false, XC>();
             break;
         case 32:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false, DECAY>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32, false, DECAY>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32, false, DECAY, false, XC>();
             break;
         case 64:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false, DECAY>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64, false, DECAY>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64, false, DECAY, false, XC>();
             break;
         default: return hipErrorInvalidValue;
     }

@@ -158,8 +158,11 @@ template <int N, typename F> __device__ LA_INLINE void static_for(F &&f) {
 // instantiation, so that the plain kernels keep their registers.  PRF: the
 // staging waves apply Performer's positive random features with as many
 // directions as input features (p.W, m = DK) instead of elu + 1 (split bf16
-// layout at CT = 64; see the staging code).
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false, bool PRF = false>
+// layout at CT = 64; see the staging code).  XCARRY (decayed MODE_AGG on bf16
+// operands, for the backward): the carry weights and the weighted values enter the MFMAs as a
+// value and its rounding remainder (see the decay factors below).
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF, bool DECAY = false, bool PRF = false,
+          bool XCARRY = false>
 __global__ void __launch_bounds__((fwd_threads<DK, DV, TI, MODE, DECAY>()))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<DK, DV, TI, CT, MODE, DECAY, PRF>())))
 la_chunk_kernel(const FwdParams p) {
@@ -220,6 +223,8 @@ la_chunk_kernel(const FwdParams p) {
     // terms) or to the phi(k) operand of the carry, so any gamma in [0, 1] stays
     // in range; the factors of full chunks are per-lane tables computed once.
     static_assert(!DECAY || MODE == MODE_CAUSAL || MODE == MODE_AGG, "decay: causal chunk loop and its aggregate");
+    static_assert(!XCARRY || (DECAY && MODE == MODE_AGG && sizeof(TI) == 2),
+                  "value-plus-remainder carry: decayed aggregate on bf16 operands");
     constexpr bool decay = DECAY;
     const float gam = decay ? p.gamma[bh % p.H] : 1.0f;
     const float lg_gam = decay ? __builtin_log2f(gam) : 0.0f;  // -inf for gamma = 0
@@ -568,11 +573,22 @@ la_chunk_kernel(const FwdParams p) {
     //             gamma^(16 D + pp - 4g - r), zero above the diagonal;
     //   dcwf[s]   carry weights of the tokens of token K step s of a full chunk,
     //             gamma^(CT - 1 - token), as an operand (slot t: the token of
-    //             the split assignment).
+    //             the split assignment).  With XCARRY the weights are recomputed
+    //             in fp32 per step instead (fewer registers than a table), and
+    //             both they and the weighted values enter the carry as a bf16
+    //             value plus its bf16 remainder.
+    // The backward takes its segment states from this aggregate.  There the
+    // per-token e = -(g . out) den meets g . v in dk and the two cancel to a
+    // small part of either under a fast decay, so errors of the carried state
+    // reach dk magnified.  With the weights and the weighted values rounded to
+    // bf16 once, each carried term has a relative error up to 2^-9; as value
+    // plus remainder, about 2^-17.  The forward's output needs no more than the
+    // single rounding.
     constexpr bool decay_out = decay && NEED_Q;
+    constexpr bool DLO = XCARRY;
     float dfq[decay_out ? NB : 1];
     float dsc[decay_out ? NB : 1][4];
-    Frag<TC> dcwf[decay ? NP : 1];
+    Frag<TC> dcwf[decay && !DLO ? NP : 1];
     if constexpr (decay_out) {
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
@@ -586,7 +602,7 @@ la_chunk_kernel(const FwdParams p) {
     }
     // token of slot t in token K step s (split assignment)
     auto slot_token = [&](int s, int t) { return 32 * s + (t < 4 ? 4 * g + t : 16 + 4 * g + t - 4); };
-    if constexpr (decay) {
+    if constexpr (decay && !DLO) {
 #pragma unroll
         for (int s = 0; s < NP; ++s)
 #pragma unroll
@@ -851,7 +867,9 @@ la_chunk_kernel(const FwdParams p) {
         }
         if (NEED_K && has_cols) {
             const float *sw = reinterpret_cast<const float *>(buf + T::OFF_W);
-#pragma unroll
+            // (one token step at a time with the value-plus-remainder carry:
+            // unrolled, its operands of both steps spill at d = 64)
+#pragma unroll(DLO ? 1 : NP)
             for (int s = 0; s < NP; ++s) {
                 Frag<TC> fkt[NE];
                 // z weights over this step's tokens (split assignment), as a
@@ -865,7 +883,15 @@ la_chunk_kernel(const FwdParams p) {
                         fw_lo.set(t, x - fw.get(t));
                     }
                 }
-                if constexpr (decay) {  // carry weights of this step's tokens
+                float cw[DLO ? 8 : 1];  // fp32 carry weights (DLO)
+                if constexpr (DLO) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        cw[t] = slot_token(s, t) < crows ? gpow(crows - 1 - slot_token(s, t)) : 0.0f;
+                        fw.set(t, cw[t]);
+                        fw_lo.set(t, cw[t] - fw.get(t));
+                    }
+                } else if constexpr (decay) {  // carry weights of this step's tokens
                     if (crows == CT) {
                         fw = dcwf[s];
                     } else {
@@ -878,20 +904,30 @@ la_chunk_kernel(const FwdParams p) {
                 for (int E = 0; E < NE; ++E) {
                     lds_frag_tr(fkt[E], sk, T::LQ, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * E, pp);
                     accZ[E] = mma(fkt[E], fw, accZ[E]);
-                    if (weighted && sizeof(TC) == 2) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
+                    if ((weighted && sizeof(TC) == 2) || DLO) accZ[E] = mma(fkt[E], fw_lo, accZ[E]);
                 }
 #pragma unroll
                 for (int cs = 0; cs < CBW; ++cs) {
                     const int cb = wave + 4 * cs;
                     if (col_ok(cs)) {
-                        Frag<TC> fv;
+                        Frag<TC> fv, fv_lo;
                         lds_frag_tr(fv, sv, T::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cb, pp);
-                        if constexpr (decay) {
+                        if constexpr (DLO) {
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) {
+                                const float x = fv.get(t) * cw[t];
+                                fv.set(t, x);
+                                fv_lo.set(t, x - fv.get(t));
+                            }
+                        } else if constexpr (decay) {
 #pragma unroll
                             for (int t = 0; t < 8; ++t) fv.set(t, fv.get(t) * fw.get(t));
                         }
 #pragma unroll
-                        for (int E = 0; E < NE; ++E) accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
+                        for (int E = 0; E < NE; ++E) {
+                            accS[cs][E] = mma(fkt[E], fv, accS[cs][E]);
+                            if constexpr (DLO) accS[cs][E] = mma(fkt[E], fv_lo, accS[cs][E]);
+                        }
                     }
                 }
             }

@@ -11,10 +11,11 @@
 namespace la {
 
 // Resident workgroups of one instantiation of the chunk kernel (cached).
-template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool DECAY = false, bool PRF = false>
+template <int DK, int DV, typename TI, int MODE, int CT, bool OBF = false, bool DECAY = false, bool PRF = false,
+          bool XCARRY = false>
 long chunk_resident() {
     static OccCache cache;
-    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY, PRF>),
+    return resident_workgroups(reinterpret_cast<const void *>(&la_chunk_kernel<DK, DV, TI, MODE, CT, OBF, DECAY, PRF, XCARRY>),
                                cache, fwd_threads<DK, DV, TI, MODE, DECAY>());
 }
 
