@@ -869,7 +869,8 @@ la_chunk_kernel(const FwdParams p) {
             const float *sw = reinterpret_cast<const float *>(buf + T::OFF_W);
             // (one token step at a time with the value-plus-remainder carry:
             // unrolled, its operands of both steps spill at d = 64)
-#pragma unroll(DLO ? 1 : NP)
+            constexpr int kCarryUnroll = DLO ? 1 : NP;
+#pragma unroll kCarryUnroll
             for (int s = 0; s < NP; ++s) {
                 Frag<TC> fkt[NE];
                 // z weights over this step's tokens (split assignment), as a
