@@ -267,7 +267,9 @@ la_status la_bwd_noncausal(const void *q, const void *k, const void *v, const vo
  * [B][H][N][m] in the input type and run the chunked kernels with the
  * identity map over m features.  The backward keeps phi(q), phi(k), dphi(q),
  * dphi(k) in the workspace in fp32 and carries dphi back through the map:
- * dx = sum_r dphi_r phi_r(x) (w_r - x).  An unknown fm, or m or d_k outside
+ * dx = sum_r dphi_r phi_r(x) (w_r - x); its cumulative sums multiply fp32
+ * operands for LA_F32 inputs and, for LA_BF16 inputs, operands held as a bf16
+ * value plus its bf16 remainder (about 16 bits).  An unknown fm, or m or d_k outside
  * {32, 64, 128} with LA_PHI_PRF, returns LA_ERR_UNSUPPORTED; a NULL W with
  * LA_PHI_PRF returns LA_ERR_NULL_PTR.
  */

@@ -56,6 +56,8 @@
 // times an odd number; each pattern is then free of bank conflicts.
 #pragma once
 
+#include <type_traits>
+
 #include "la_device.hpp"
 
 namespace la {
@@ -161,7 +163,8 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
     }
 
     // Rows [0, CM) of the tile (leading dimension LD) from the registers; zero
-    // past nrows (FULL: the caller knows nrows == CM).
+    // past nrows (FULL: the caller knows nrows == CM).  bf16-pair tiles take
+    // the loaded fp32 words as value-plus-remainder words.
     template <int LD, bool FULL>
     __device__ __forceinline__ void store(TI *tile, int nrows, int tid) const {
 #pragma unroll
@@ -170,7 +173,8 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
             if (NV % NT != 0 && idx >= NV) continue;
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
-            const uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
+            uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
+            if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
             *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
         }
     }
@@ -761,7 +765,10 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                 const int e = 16 * (I - J) + 4 * g + r - pp;  // i - j
                 const bool keep = !(I == J && e < 0);
                 const float w = dec && keep ? dcy.pow(e) : 1.0f;
-                acc[r] = keep ? (is_a ? acc[r] : acc[r] + ev[r]) * av[r] * w : 0.f;
+                // bf16 pairs: g_i . v_j as the dq sweep's M tile held it, the
+                // value e_i was formed from (a lone token's g . v + e is then 0)
+                const float gv = std::is_same<TC, bf16p>::value && !is_a ? to_operand<TC>(acc[r]) : acc[r];
+                acc[r] = keep ? (is_a ? acc[r] : gv + ev[r]) * av[r] * w : 0.f;
             }
             const int off = (16 * J + pp) * SM::LM + 16 * I + 4 * g;
             if (!is_a)

@@ -124,9 +124,13 @@ hipError_t run_bwd_nc_t(const BwdDesc &d) {
     }
 }
 
-// DECAY: the causal form with a per-head decay (d.gamma non-null).
+// DECAY: the causal form with a per-head decay (d.gamma non-null).  TI =
+// bf16p: fp32 buffers whose sweeps multiply bf16 value-plus-remainder
+// operands; the prefix aggregate then runs on the fp32 data (type TA).
 template <int DK, int DV, typename TI, bool DECAY>
 hipError_t run_bwd_causal_t(const BwdDesc &d) {
+    using TA = typename std::conditional<std::is_same<TI, bf16p>::value, float, TI>::type;
+    static_assert(!DECAY || !std::is_same<TI, bf16p>::value, "bf16-pair sweeps: no decay");
     const long BH = (long)d.B * d.H;
     int Lmax = 0;
     const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);
@@ -141,21 +145,21 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
     // The prefix aggregate reuses the forward's chunk kernel at the caller's
     // chunk size (the suffix sums come from the dq sweep); decayed on bf16
     // operands, in its value-plus-remainder carry variant.
-    constexpr bool XC = DECAY && sizeof(TI) == 2;
+    constexpr bool XC = DECAY && sizeof(TA) == 2;
     void (*agg_kernel)(const FwdParams) = nullptr;
     long target_agg = 0;
-    switch (fwd_chunk<DK, DV, TI>(d.C)) {
+    switch (fwd_chunk<DK, DV, TA>(d.C)) {
         case 16:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 16, false, DECAY, false, XC>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 16, false, DECAY, false, XC>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TA, MODE_AGG, 16, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TA, MODE_AGG, 16, false, DECAY, false, XC>();
             break;
         case 32:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 32, false, DECAY, false, XC>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 32, false, DECAY, false, XC>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TA, MODE_AGG, 32, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TA, MODE_AGG, 32, false, DECAY, false, XC>();
             break;
         case 64:
-            agg_kernel = &la_chunk_kernel<DK, DV, TI, MODE_AGG, 64, false, DECAY, false, XC>;
-            target_agg = chunk_resident<DK, DV, TI, MODE_AGG, 64, false, DECAY, false, XC>();
+            agg_kernel = &la_chunk_kernel<DK, DV, TA, MODE_AGG, 64, false, DECAY, false, XC>;
+            target_agg = chunk_resident<DK, DV, TA, MODE_AGG, 64, false, DECAY, false, XC>();
             break;
         default: return hipErrorInvalidValue;
     }
@@ -193,7 +197,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
         a.v = d.v;
         a.seg_out = pre;
         a.seg_base = 0;
-        agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TI, MODE_AGG, DECAY>(), 0, d.stream>>>(a);
+        agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TA, MODE_AGG, DECAY>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
             hipSuccess)
@@ -244,17 +248,34 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
 
 template <int DK, int DV, typename TI>
 hipError_t run_bwd_t(const BwdDesc &d) {
-    if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);
-    return d.gamma ? run_bwd_causal_t<DK, DV, TI, true>(d) : run_bwd_causal_t<DK, DV, TI, false>(d);
+    if constexpr (std::is_same<TI, bf16p>::value) {
+        if (d.noncausal || d.gamma) return hipErrorInvalidValue;
+        return run_bwd_causal_t<DK, DV, TI, false>(d);
+    } else {
+        if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);
+        return d.gamma ? run_bwd_causal_t<DK, DV, TI, true>(d) : run_bwd_causal_t<DK, DV, TI, false>(d);
+    }
+}
+
+// bf16-pair sweeps are built for the widths the random features give the state
+// (m in {32, 64, 128}).
+template <int DK, int DV>
+hipError_t run_bwd_pair(const BwdDesc &d) {
+    if constexpr (DK >= 32) return run_bwd_t<DK, DV, bf16p>(d);
+    else return hipErrorInvalidValue;
 }
 
 template <int DK>
 hipError_t run_bwd_dk(const BwdDesc &d) {
     switch (d.DV) {
-        case 16: return d.in_bf16 ? run_bwd_t<DK, 16, __bf16>(d) : run_bwd_t<DK, 16, float>(d);
-        case 32: return d.in_bf16 ? run_bwd_t<DK, 32, __bf16>(d) : run_bwd_t<DK, 32, float>(d);
-        case 64: return d.in_bf16 ? run_bwd_t<DK, 64, __bf16>(d) : run_bwd_t<DK, 64, float>(d);
-        case 128: return d.in_bf16 ? run_bwd_t<DK, 128, __bf16>(d) : run_bwd_t<DK, 128, float>(d);
+        case 16: return d.pair_ops ? run_bwd_pair<DK, 16>(d)
+                          : d.in_bf16 ? run_bwd_t<DK, 16, __bf16>(d) : run_bwd_t<DK, 16, float>(d);
+        case 32: return d.pair_ops ? run_bwd_pair<DK, 32>(d)
+                          : d.in_bf16 ? run_bwd_t<DK, 32, __bf16>(d) : run_bwd_t<DK, 32, float>(d);
+        case 64: return d.pair_ops ? run_bwd_pair<DK, 64>(d)
+                          : d.in_bf16 ? run_bwd_t<DK, 64, __bf16>(d) : run_bwd_t<DK, 64, float>(d);
+        case 128: return d.pair_ops ? run_bwd_pair<DK, 128>(d)
+                          : d.in_bf16 ? run_bwd_t<DK, 128, __bf16>(d) : run_bwd_t<DK, 128, float>(d);
         default: return hipErrorInvalidValue;
     }
 }

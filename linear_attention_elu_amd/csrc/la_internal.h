@@ -59,6 +59,7 @@ struct BwdDesc {
     int noncausal;  // gradient of the non-causal form (full sums)
     int phi_id;     // feature map: 0 = elu + 1, 1 = identity
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
+    int pair_ops;  // fp32 buffers, sweep products on bf16 value-plus-remainder operands (causal, no decay)
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a

@@ -503,8 +503,11 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     if (fm == LA_PHI_ELU1) return la_bwd_causal(q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in, ws, ws_bytes, stream);
     la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, mf, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream, 0, 1};
     if (fm == LA_PHI_IDENTITY) return la::from_hip(la::run_bwd(d));
-    // Random features: the sweeps run in fp32 on fp32 features (and fp32 v, dO
-    // for bf16 inputs), so that dphi reaches the chain rule with fp32 accuracy.
+    // Random features: the sweeps read fp32 features (and fp32 copies of v and
+    // dO for bf16 inputs) and write dphi in fp32, so that the chain rule gets
+    // it far more accurate than a bf16 rounding of the features would leave it.
+    // fp32 inputs: fp32 products.  bf16 inputs: products of bf16 value-plus-
+    // remainder pairs (about 16 bits), four bf16 MFMAs each.
     const FmLayout l = fm_layout(true, B, H, N, m, d_v, in, 0);
     const long BH = (long)B * H;
     const bool bf = in == LA_BF16;
@@ -524,6 +527,7 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     d.dq = at(ws, l.dfq);  // the sweeps return dphi(q), dphi(k) (identity map)
     d.dk = at(ws, l.dfk);
     d.in_bf16 = 0;
+    d.pair_ops = bf ? 1 : 0;
     d.ws = reinterpret_cast<float *>(at(ws, l.inner));
     if ((e = la::run_bwd(d)) != hipSuccess) return la::from_hip(e);
     if (bf && (e = la::launch_convert(false, at(ws, l.dv32), dv, BH * N * (long)d_v, stream)) != hipSuccess)
