@@ -164,9 +164,10 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
 
     // Rows [0, CM) of the tile (leading dimension LD) from the registers; zero
     // past nrows (FULL: the caller knows nrows == CM).  bf16-pair tiles take
-    // the loaded fp32 words as value-plus-remainder words.
-    template <int LD, bool FULL>
-    __device__ __forceinline__ void store(TI *tile, int nrows, int tid) const {
+    // loaded fp32 words as value-plus-remainder words, and loaded bf16 values
+    // as pair words with a zero remainder (eight words from each vector).
+    template <int LD, bool FULL, typename TT>
+    __device__ __forceinline__ void store(TT *tile, int nrows, int tid) const {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int idx = tid + it * NT;
@@ -174,8 +175,15 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
             uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
-            if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
-            *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
+            if constexpr (std::is_same<TT, bf16p>::value && std::is_same<TI, __bf16>::value) {
+                uint4 *dst = reinterpret_cast<uint4 *>(tile + row * LD + col);
+                dst[0] = make_uint4(w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16);
+                dst[1] = make_uint4(w.z & 0xffffu, w.z >> 16, w.w & 0xffffu, w.w >> 16);
+            } else {
+                static_assert(std::is_same<TT, TI>::value, "staging: tile of the loaded type, or bf16 into pairs");
+                if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
+                *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
+            }
         }
     }
 };
@@ -302,7 +310,9 @@ la_bwd_dq_kernel(const BwdParams p) {
     frag_ones(ones);
 
     RowRegs<TI, DK, kBwdThreads, SM::CM> xk, xq;
-    RowRegs<TI, DV, kBwdThreads, SM::CM> xv, xg;
+    // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
+    using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
+    RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
@@ -678,7 +688,9 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     if (has_e) refresh();
 
     RowRegs<TI, DK, kBwdThreads, SM::CM> xq, xk;
-    RowRegs<TI, DV, kBwdThreads, SM::CM> xv, xg;
+    // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
+    using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
+    RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
     float xe = 0.f, xa = 0.f;  // e and a of token tid (tid < CM)
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
@@ -873,7 +885,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                             acc = mma(frt[s], fk, acc);
                         }
                     }
-                    if (valid) store4<TI>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
+                    if (valid) store4<TG>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
                 }
             }
         }

@@ -125,8 +125,9 @@ hipError_t run_bwd_nc_t(const BwdDesc &d) {
 }
 
 // DECAY: the causal form with a per-head decay (d.gamma non-null).  TI =
-// bf16p: fp32 buffers whose sweeps multiply bf16 value-plus-remainder
-// operands; the prefix aggregate then runs on the fp32 data (type TA).
+// bf16p: sweeps that multiply bf16 value-plus-remainder operands, on fp32 q,
+// k and bf16 v, dO; the prefix aggregate then runs on fp32 k and d.v_agg
+// (type TA).
 template <int DK, int DV, typename TI, bool DECAY>
 hipError_t run_bwd_causal_t(const BwdDesc &d) {
     using TA = typename std::conditional<std::is_same<TI, bf16p>::value, float, TI>::type;
@@ -194,7 +195,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
         // prefix sums: the last segment's own fine segments are not needed
         const int nagg = (Pc - 1) * mult;
         a.k = d.k;
-        a.v = d.v;
+        a.v = std::is_same<TI, bf16p>::value ? d.v_agg : d.v;
         a.seg_out = pre;
         a.seg_base = 0;
         agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TA, MODE_AGG, DECAY>(), 0, d.stream>>>(a);
@@ -249,7 +250,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
 template <int DK, int DV, typename TI>
 hipError_t run_bwd_t(const BwdDesc &d) {
     if constexpr (std::is_same<TI, bf16p>::value) {
-        if (d.noncausal || d.gamma) return hipErrorInvalidValue;
+        if (d.noncausal || d.gamma || !d.v_agg) return hipErrorInvalidValue;
         return run_bwd_causal_t<DK, DV, TI, false>(d);
     } else {
         if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);

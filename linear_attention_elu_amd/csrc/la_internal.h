@@ -59,7 +59,11 @@ struct BwdDesc {
     int noncausal;  // gradient of the non-causal form (full sums)
     int phi_id;     // feature map: 0 = elu + 1, 1 = identity
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
-    int pair_ops;  // fp32 buffers, sweep products on bf16 value-plus-remainder operands (causal, no decay)
+    // Sweep products on bf16 value-plus-remainder operands (causal, no decay):
+    // q, k, dq, dk fp32, v, dO, dv bf16, and v_agg the fp32 values of v for
+    // the prefix aggregate (whose products stay fp32).
+    int pair_ops;
+    const void *v_agg;
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a
@@ -120,8 +124,8 @@ constexpr int kNonCausalChunk = 64;
 enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2 };
 hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const void *f, const void *df, void *out,
                       long BH, int N, int H, int DK, int M, hipStream_t stream);
-// n values bf16 -> fp32 (to_f32) or fp32 -> bf16 (round to nearest even).
-hipError_t launch_convert(bool to_f32, const void *a, void *b, long n, hipStream_t stream);
+// n values bf16 -> fp32.
+hipError_t launch_convert(const void *a, void *b, long n, hipStream_t stream);
 
 // Argument checks of the causal forward entry points (all but the workspace),
 // before any HIP call; the status the entry point returns.

@@ -221,33 +221,19 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
     }
 }
 
-// Element-wise type conversion of n values (bf16 <-> fp32 staging of the
-// random-feature backward), eight per thread and step with 16-byte accesses
-// (both buffers 16-byte aligned); the last n % 8 values one by one.
-template <typename TA, typename TB>
-__global__ void __launch_bounds__(256) la_convert_kernel(const TA *__restrict__ a, TB *__restrict__ b, long n) {
+// bf16 -> fp32 copy of n values (v for the random-feature backward's prefix
+// aggregate), eight per thread and step with 16-byte accesses (both buffers
+// 16-byte aligned); the last n % 8 values one by one.
+__global__ void __launch_bounds__(256) la_convert_kernel(const __bf16 *__restrict__ a, float *__restrict__ b, long n) {
     const long nv = n / 8;
     for (long i = blockIdx.x * 256L + threadIdx.x; i < nv; i += (long)gridDim.x * 256L) {
         float x[8];
-        if constexpr (sizeof(TA) == 2) {
-            const uint4 u = load_stream16(a + 8 * i);
-            unpack16(u, x, __bf16());
-        } else {
-            const uint4 u0 = load_stream16(a + 8 * i), u1 = load_stream16(a + 8 * i + 4);
-            x[0] = __uint_as_float(u0.x), x[1] = __uint_as_float(u0.y), x[2] = __uint_as_float(u0.z);
-            x[3] = __uint_as_float(u0.w), x[4] = __uint_as_float(u1.x), x[5] = __uint_as_float(u1.y);
-            x[6] = __uint_as_float(u1.z), x[7] = __uint_as_float(u1.w);
-        }
-        if constexpr (sizeof(TB) == 2) {
-            const uint2 lo = pack_bf16x4(f32x4{x[0], x[1], x[2], x[3]}), hi = pack_bf16x4(f32x4{x[4], x[5], x[6], x[7]});
-            *reinterpret_cast<uint4 *>(b + 8 * i) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        } else {
-            *reinterpret_cast<f32x4 *>(b + 8 * i) = f32x4{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<f32x4 *>(b + 8 * i + 4) = f32x4{x[4], x[5], x[6], x[7]};
-        }
+        unpack16(load_stream16(a + 8 * i), x, __bf16());
+        *reinterpret_cast<f32x4 *>(b + 8 * i) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4 *>(b + 8 * i + 4) = f32x4{x[4], x[5], x[6], x[7]};
     }
     for (long i = 8 * nv + blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256L)
-        b[i] = static_cast<TB>(static_cast<float>(a[i]));
+        b[i] = static_cast<float>(a[i]);
 }
 
 template <typename TC, int DK, int M>
@@ -300,17 +286,12 @@ hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const v
     return launch_prf_any(bf16, what, x, W, f, df, out, BH, N, H, DK, M, stream);
 }
 
-hipError_t launch_convert(bool to_f32, const void *a, void *b, long n, hipStream_t stream) {
+hipError_t launch_convert(const void *a, void *b, long n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     long blocks = (n / 8 + 255) / 256;  // eight values per thread
     if (blocks < 1) blocks = 1;
     if (blocks > 8192) blocks = 8192;
-    if (to_f32)
-        la_convert_kernel<__bf16, float><<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const __bf16 *>(a),
-                                                                               static_cast<float *>(b), n);
-    else
-        la_convert_kernel<float, __bf16><<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const float *>(a),
-                                                                               static_cast<__bf16 *>(b), n);
+    la_convert_kernel<<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const __bf16 *>(a), static_cast<float *>(b), n);
     return hipGetLastError();
 }
 
@@ -327,10 +308,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the random map.  Forward: phi(q), phi(k) as [BH][N][m] in the
 // input type, then the inner call's workspace.  Backward: phi(q), phi(k),
-// dphi(q), dphi(k) in fp32 and, for bf16 inputs, fp32 copies of v and dO and
-// an fp32 dv, then the inner (fp32) backward's workspace.
+// dphi(q), dphi(k) in fp32 and, for bf16 inputs, an fp32 copy of v (for the
+// prefix aggregate), then the inner backward's workspace.
 struct FmLayout {
-    size_t fq, fk, dfq, dfk, v32, g32, dv32, inner, total;
+    size_t fq, fk, dfq, dfk, v32, inner, total;
 };
 FmLayout fm_layout(bool bwd, int B, int H, int N, int m, int d_v, int in, size_t inner_bytes) {
     const size_t th = (size_t)B * H * N;
@@ -347,11 +328,7 @@ FmLayout fm_layout(bool bwd, int B, int H, int N, int m, int d_v, int in, size_t
     if (bwd) {
         l.dfq = take(th * m * 4);
         l.dfk = take(th * m * 4);
-        if (in == LA_BF16) {
-            l.v32 = take(th * d_v * 4);
-            l.g32 = take(th * d_v * 4);
-            l.dv32 = take(th * d_v * 4);
-        }
+        if (in == LA_BF16) l.v32 = take(th * d_v * 4);
     }
     l.inner = off;
     l.total = off + inner_bytes;
@@ -503,35 +480,31 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     if (fm == LA_PHI_ELU1) return la_bwd_causal(q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in, ws, ws_bytes, stream);
     la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, mf, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream, 0, 1};
     if (fm == LA_PHI_IDENTITY) return la::from_hip(la::run_bwd(d));
-    // Random features: the sweeps read fp32 features (and fp32 copies of v and
-    // dO for bf16 inputs) and write dphi in fp32, so that the chain rule gets
-    // it far more accurate than a bf16 rounding of the features would leave it.
-    // fp32 inputs: fp32 products.  bf16 inputs: products of bf16 value-plus-
-    // remainder pairs (about 16 bits), four bf16 MFMAs each.
+    // Random features: the sweeps read fp32 features and write dphi in fp32,
+    // so that the chain rule gets it far more accurate than a bf16 rounding of
+    // the features would leave it.  fp32 inputs: fp32 products.  bf16 inputs:
+    // products of bf16 value-plus-remainder pairs (about 16 bits, four bf16
+    // MFMAs each) on the bf16 v and dO as given, dv written in bf16; only the
+    // prefix aggregate, whose products stay fp32, reads an fp32 copy of v.
     const FmLayout l = fm_layout(true, B, H, N, m, d_v, in, 0);
     const long BH = (long)B * H;
     const bool bf = in == LA_BF16;
     hipError_t e = la::launch_prf(bf, la::PRF_PHI_F32, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k, m, stream);
     if (e == hipSuccess)
         e = la::launch_prf(bf, la::PRF_PHI_F32, k, W, nullptr, nullptr, at(ws, l.fk), BH, N, H, d_k, m, stream);
-    if (e == hipSuccess && bf) e = la::launch_convert(true, v, at(ws, l.v32), BH * N * (long)d_v, stream);
-    if (e == hipSuccess && bf) e = la::launch_convert(true, dO, at(ws, l.g32), BH * N * (long)d_v, stream);
+    if (e == hipSuccess && bf) e = la::launch_convert(v, at(ws, l.v32), BH * N * (long)d_v, stream);
     if (e != hipSuccess) return la::from_hip(e);
     d.q = at(ws, l.fq);
     d.k = at(ws, l.fk);
-    if (bf) {
-        d.v = at(ws, l.v32);
-        d.dO = at(ws, l.g32);
-        d.dv = at(ws, l.dv32);
-    }
     d.dq = at(ws, l.dfq);  // the sweeps return dphi(q), dphi(k) (identity map)
     d.dk = at(ws, l.dfk);
     d.in_bf16 = 0;
-    d.pair_ops = bf ? 1 : 0;
+    if (bf) {
+        d.pair_ops = 1;
+        d.v_agg = at(ws, l.v32);
+    }
     d.ws = reinterpret_cast<float *>(at(ws, l.inner));
     if ((e = la::run_bwd(d)) != hipSuccess) return la::from_hip(e);
-    if (bf && (e = la::launch_convert(false, at(ws, l.dv32), dv, BH * N * (long)d_v, stream)) != hipSuccess)
-        return la::from_hip(e);
     e = la::launch_prf(bf, la::PRF_VJP, q, W, at(ws, l.fq), at(ws, l.dfq), dq, BH, N, H, d_k, m, stream);
     if (e == hipSuccess)
         e = la::launch_prf(bf, la::PRF_VJP, k, W, at(ws, l.fk), at(ws, l.dfk), dk, BH, N, H, d_k, m, stream);
