@@ -125,39 +125,47 @@ __device__ __forceinline__ void lower_block(int b, int &I, int &J) {
 // the chunk's end are clamped to its last row and zeroed at the store), which
 // keeps the wait before the store exact.
 template <typename TI, int D, int NT, int CM> struct RowRegs {
+    static constexpr bool HALVES = std::is_same<TI, bf16h>::value;  // two bf16 planes, `plane` elements apart
     static constexpr int VEC = Store<TI>::VEC;
-    static constexpr int VPR = D / VEC;  // 16-byte vectors per row
+    static constexpr int VPR = D / VEC;  // 16-byte vectors per row (of one plane)
     static constexpr int NV = CM * VPR;
     static constexpr int NIT = (NV + NT - 1) / NT;
     uint4 u[NIT];
+    uint4 ul[HALVES ? NIT : 1];  // the remainder plane's vectors
 
-    __device__ __forceinline__ void load(const void *src, long row_base, int r0, int nrows, int tid) {
+    __device__ __forceinline__ void load(const void *src, long row_base, int r0, int nrows, int tid, long plane = 0) {
+        constexpr long ES = HALVES ? 2 : (long)sizeof(TI);  // bytes per element of a plane
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int idx = tid + it * NT;
             const int row = min(idx / VPR, nrows - 1);
             const int col = (idx % VPR) * VEC;
-            u[it] = load_stream16(static_cast<const char *>(src) +
-                                  ((row_base + r0 + row) * D + col) * (long)sizeof(TI));
+            const char *at = static_cast<const char *>(src) + ((row_base + r0 + row) * D + col) * ES;
+            u[it] = load_stream16(at);
+            if constexpr (HALVES) ul[it] = load_stream16(at + plane * ES);
         }
     }
 
     // phi of the loaded values, in place (16-byte vectors of TI); nothing for
     // the identity map.
     __device__ __forceinline__ void apply_phi(bool ident) {
-        if (ident) return;
+        if constexpr (HALVES) {
+            return;  // features given (identity map only)
+        } else {
+            if (ident) return;
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            float x[VEC];
-            unpack16(u[it], x, TI());
-            if constexpr (sizeof(TI) == 2) {
-                const f32x4 a = {phi(x[0]), phi(x[1]), phi(x[2]), phi(x[3])};
-                const f32x4 b = {phi(x[4]), phi(x[5]), phi(x[6]), phi(x[7])};
-                const uint2 pa = pack_bf16x4(a), pb = pack_bf16x4(b);
-                u[it] = make_uint4(pa.x, pa.y, pb.x, pb.y);
-            } else {
-                u[it] = make_uint4(__float_as_uint(phi(x[0])), __float_as_uint(phi(x[1])),
-                                   __float_as_uint(phi(x[2])), __float_as_uint(phi(x[3])));
+            for (int it = 0; it < NIT; ++it) {
+                float x[VEC];
+                unpack16(u[it], x, TI());
+                if constexpr (sizeof(TI) == 2) {
+                    const f32x4 a = {phi(x[0]), phi(x[1]), phi(x[2]), phi(x[3])};
+                    const f32x4 b = {phi(x[4]), phi(x[5]), phi(x[6]), phi(x[7])};
+                    const uint2 pa = pack_bf16x4(a), pb = pack_bf16x4(b);
+                    u[it] = make_uint4(pa.x, pa.y, pb.x, pb.y);
+                } else {
+                    u[it] = make_uint4(__float_as_uint(phi(x[0])), __float_as_uint(phi(x[1])),
+                                       __float_as_uint(phi(x[2])), __float_as_uint(phi(x[3])));
+                }
             }
         }
     }
@@ -179,6 +187,15 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
                 uint4 *dst = reinterpret_cast<uint4 *>(tile + row * LD + col);
                 dst[0] = make_uint4(w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16);
                 dst[1] = make_uint4(w.z & 0xffffu, w.z >> 16, w.w & 0xffffu, w.w >> 16);
+            } else if constexpr (HALVES) {
+                static_assert(std::is_same<TT, bf16p>::value, "bf16 planes stage into pair tiles");
+                // pair word = value half | remainder half << 16, element by element
+                const uint4 l = (FULL || row < nrows) ? ul[it] : make_uint4(0, 0, 0, 0);
+                uint4 *dst = reinterpret_cast<uint4 *>(tile + row * LD + col);
+                dst[0] = make_uint4(__builtin_amdgcn_perm(l.x, w.x, 0x05040100u), __builtin_amdgcn_perm(l.x, w.x, 0x07060302u),
+                                    __builtin_amdgcn_perm(l.y, w.y, 0x05040100u), __builtin_amdgcn_perm(l.y, w.y, 0x07060302u));
+                dst[1] = make_uint4(__builtin_amdgcn_perm(l.z, w.z, 0x05040100u), __builtin_amdgcn_perm(l.z, w.z, 0x07060302u),
+                                    __builtin_amdgcn_perm(l.w, w.w, 0x05040100u), __builtin_amdgcn_perm(l.w, w.w, 0x07060302u));
             } else {
                 static_assert(std::is_same<TT, TI>::value, "staging: tile of the loaded type, or bf16 into pairs");
                 if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
@@ -309,15 +326,18 @@ la_bwd_dq_kernel(const BwdParams p) {
     Frag<TC> ones;
     frag_ones(ones);
 
-    RowRegs<TI, DK, kBwdThreads, SM::CM> xk, xq;
+    // q, k: two bf16 planes (value, remainder) for bf16-pair sweeps
+    using TQ = typename std::conditional<std::is_same<TI, bf16p>::value, bf16h, TI>::type;
+    const long fplane = (long)gridDim.x * N * DK;  // elements per plane
+    RowRegs<TQ, DK, kBwdThreads, SM::CM> xk, xq;
     // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
     using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
     RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        if constexpr (!NC) xk.load(p.k, bh * N, r0, nrows, tid);
-        xq.load(p.q, bh * N, r0, nrows, tid);
+        if constexpr (!NC) xk.load(p.k, bh * N, r0, nrows, tid, fplane);
+        xq.load(p.q, bh * N, r0, nrows, tid, fplane);
         if constexpr (!NC) xv.load(p.v, bh * N, r0, nrows, tid);
         xg.load(p.g, bh * N, r0, nrows, tid);
     };
@@ -687,7 +707,9 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     };
     if (has_e) refresh();
 
-    RowRegs<TI, DK, kBwdThreads, SM::CM> xq, xk;
+    using TQ = typename std::conditional<std::is_same<TI, bf16p>::value, bf16h, TI>::type;
+    const long fplane = (long)gridDim.x * N * DK;  // elements per plane
+    RowRegs<TQ, DK, kBwdThreads, SM::CM> xq, xk;
     // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
     using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
     RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
@@ -695,8 +717,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
-        if constexpr (!NC) xq.load(p.q, bh * N, r0, nrows, tid);
-        xk.load(p.k, bh * N, r0, nrows, tid);
+        if constexpr (!NC) xq.load(p.q, bh * N, r0, nrows, tid, fplane);
+        xk.load(p.k, bh * N, r0, nrows, tid, fplane);
         xv.load(p.v, bh * N, r0, nrows, tid);
         if constexpr (!NC) xg.load(p.g, bh * N, r0, nrows, tid);
         if (!NC && tid < SM::CM) {

@@ -125,13 +125,15 @@ hipError_t run_bwd_nc_t(const BwdDesc &d) {
 }
 
 // DECAY: the causal form with a per-head decay (d.gamma non-null).  TI =
-// bf16p: sweeps that multiply bf16 value-plus-remainder operands, on fp32 q,
-// k and bf16 v, dO; the prefix aggregate then runs on fp32 k and d.v_agg
-// (type TA).
+// bf16p: sweeps that multiply bf16 value-plus-remainder operands, on q and k
+// given as two bf16 planes (value, remainder) and bf16 v, dO; the prefix
+// aggregate is then the sum of two bf16 passes (type TA), one per plane of k,
+// each product of bf16 values exact in fp32.
 template <int DK, int DV, typename TI, bool DECAY>
 hipError_t run_bwd_causal_t(const BwdDesc &d) {
-    using TA = typename std::conditional<std::is_same<TI, bf16p>::value, float, TI>::type;
-    static_assert(!DECAY || !std::is_same<TI, bf16p>::value, "bf16-pair sweeps: no decay");
+    constexpr bool PAIR = std::is_same<TI, bf16p>::value;
+    using TA = typename std::conditional<PAIR, __bf16, TI>::type;
+    static_assert(!DECAY || !PAIR, "bf16-pair sweeps: no decay");
     const long BH = (long)d.B * d.H;
     int Lmax = 0;
     const int Pmax = plan_segments(BH, d.N, d.C, kMaxTargetWg, &Lmax);
@@ -195,13 +197,20 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
         // prefix sums: the last segment's own fine segments are not needed
         const int nagg = (Pc - 1) * mult;
         a.k = d.k;
-        a.v = std::is_same<TI, bf16p>::value ? d.v_agg : d.v;
+        a.v = d.v;
         a.seg_out = pre;
         a.seg_base = 0;
         agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TA, MODE_AGG, DECAY>(), 0, d.stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf)) !=
-            hipSuccess)
+        if constexpr (PAIR) {  // the remainder half of k
+            a.k = static_cast<const __bf16 *>(d.k) + BH * d.N * (long)DK;
+            a.seg_out = d.agg_lo;
+            agg_kernel<<<dim3((unsigned)BH, (unsigned)nagg), fwd_threads<DK, DV, TA, MODE_AGG, DECAY>(), 0,
+                         d.stream>>>(a);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if ((err = launch_seg_scan(pre, nullptr, nullptr, BH, Pf, DK, DV, 0, nagg, d.stream, d.gamma, d.H, Lf,
+                                   PAIR ? d.agg_lo : nullptr)) != hipSuccess)
             return err;
     }
 
@@ -250,7 +259,7 @@ hipError_t run_bwd_causal_t(const BwdDesc &d) {
 template <int DK, int DV, typename TI>
 hipError_t run_bwd_t(const BwdDesc &d) {
     if constexpr (std::is_same<TI, bf16p>::value) {
-        if (d.noncausal || d.gamma || !d.v_agg) return hipErrorInvalidValue;
+        if (d.noncausal || d.gamma || !d.agg_lo) return hipErrorInvalidValue;
         return run_bwd_causal_t<DK, DV, TI, false>(d);
     } else {
         if (d.noncausal) return run_bwd_nc_t<DK, DV, TI>(d);

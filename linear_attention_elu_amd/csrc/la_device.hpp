@@ -438,6 +438,13 @@ template <> struct Store<bf16p> {  // global buffers of bf16-pair operands hold 
     }
 };
 
+// fp32 values held as two bf16 planes (value, remainder) of the same layout;
+// staged into bf16-pair tiles.
+struct bf16h {};
+template <> struct Store<bf16h> {
+    static constexpr int VEC = 8;  // elements per 16-byte vector of one plane
+};
+
 template <> struct Store<__bf16> {
     static constexpr int VEC = 8;
     __device__ __forceinline__ static float load(const void *p, long i) {

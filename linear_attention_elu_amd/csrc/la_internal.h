@@ -60,10 +60,12 @@ struct BwdDesc {
     int phi_id;     // feature map: 0 = elu + 1, 1 = identity
     const float *gamma;  // causal only: per-head decay [H] (device), or null for none
     // Sweep products on bf16 value-plus-remainder operands (causal, no decay):
-    // q, k, dq, dk fp32, v, dO, dv bf16, and v_agg the fp32 values of v for
-    // the prefix aggregate (whose products stay fp32).
+    // q and k as two bf16 planes each (value, remainder: [2][B*H][N][DK]),
+    // dq and dk fp32, v, dO and dv bf16.  The prefix aggregate then runs once
+    // per plane of k on bf16 operands, the second pass writing its segment
+    // sums to agg_lo (the size of the prefix workspace).
     int pair_ops;
-    const void *v_agg;
+    float *agg_lo;
 };
 
 // Split of each (batch, head) sequence into P segments of L tokens (L a
@@ -99,9 +101,11 @@ inline long state_floats(int DK, int DV) { return (long)DK * DV + DK; }
 // With gamma non-null, the segments hold L tokens each and decay by
 // gamma[bh % H] per token: mode 0, entering(s) = gamma^L entering(s - 1) +
 // aggregate(s - 1); mode 2, after(s) = aggregate(s + 1) + gamma^L after(s + 1).
+// add (mode 0, nullable): a second buffer of aggregates in ws's layout, added
+// to ws's (the two halves of a split aggregate).
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
                            int mode, int lim, hipStream_t stream, const float *gamma = nullptr, int H = 1,
-                           int L = 0);
+                           int L = 0, const float *add = nullptr);
 
 // Shared argument predicates and sizes of the entry points (la_api.cpp).
 bool dim_ok(int d);
@@ -118,14 +122,15 @@ constexpr int kNonCausalChunk = 64;
 // The random-feature map and its backward (la_prf.hip), x [BH][N][DK] and the
 // directions W [H][M][DK] in the input type:
 //   PRF_PHI      out = phi(x) [BH][N][M] in the input type;
-//   PRF_PHI_F32  out = phi(x) in fp32;
+//   PRF_PHI_F32  out = phi(x) in fp32 (out may be null), and with halves
+//                non-null phi(x) as its bf16 value (plane 0) and bf16
+//                remainder (plane 1), bf16 [2][BH][N][M];
 //   PRF_VJP      out = dx [BH][N][DK] (input type) from x, f = phi(x) and
-//                df = dphi, both fp32.
-enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2 };
+//                df = dphi, both fp32;
+//   PRF_VJP_PLANES  the same with f = phi(x) as the two bf16 planes.
+enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2, PRF_VJP_PLANES = 3 };
 hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const void *f, const void *df, void *out,
-                      long BH, int N, int H, int DK, int M, hipStream_t stream);
-// n values bf16 -> fp32.
-hipError_t launch_convert(const void *a, void *b, long n, hipStream_t stream);
+                      long BH, int N, int H, int DK, int M, hipStream_t stream, void *halves = nullptr);
 
 // Argument checks of the causal forward entry points (all but the workspace),
 // before any HIP call; the status the entry point returns.

@@ -93,7 +93,8 @@ template <typename TC> __device__ __forceinline__ f32x4 load4(const TC *p) {
 // issued before W is staged.
 template <typename TC, typename TO, int DK, int M>
 __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
-                                                             TO *__restrict__ out, int N, int H) {
+                                                             TO *__restrict__ out, __bf16 *__restrict__ halves, int N,
+                                                             int H) {
     constexpr int LW = prf_ld<TC, DK>();
     constexpr int NF = M / 16, NS = DK / 32;
     __shared__ __attribute__((aligned(16))) TC sw[M * LW];
@@ -134,13 +135,20 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
         }
         nx = sum_over_groups(nx);
         if (t0 + pp < N) {
-            TO *orow = out + (bh * N + t0 + pp) * (long)M;
 #pragma unroll
             for (int F = 0; F < NF; ++F) {
                 f32x4 f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) f[r] = __expf(acc[F][r] - 0.5f * nx) * scale;
-                store4_to(orow + 16 * F + 4 * g, f);
+                if (out) store4_to(out + (bh * N + t0 + pp) * (long)M + 16 * F + 4 * g, f);  // uniform
+                if (halves) {  // uniform: phi as its bf16 value and bf16 remainder, two planes
+                    const long at = (bh * N + t0 + pp) * (long)M + 16 * F + 4 * g;
+                    const uint2 hv = pack_bf16x4(f);
+                    const f32x4 h = {__uint_as_float(hv.x << 16), __uint_as_float(hv.x & 0xffff0000u),
+                                     __uint_as_float(hv.y << 16), __uint_as_float(hv.y & 0xffff0000u)};
+                    *reinterpret_cast<uint2 *>(halves + at) = hv;
+                    *reinterpret_cast<uint2 *>(halves + (long)gridDim.x * N * M + at) = pack_bf16x4(f - h);
+                }
             }
         }
     }
@@ -155,9 +163,9 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
 // of dphi that is small against its row but large against a small entry is
 // multiplied by a large phi_r(x).  The token blocks are pipelined as in
 // la_prf_kernel (phi, dphi and the x elements of the epilogue in flight).
-template <typename TC, int DK, int M>
+template <typename TC, int DK, int M, bool PH = false>  // PH: phi_x as two bf16 planes (value, remainder)
 __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
-                                                                 const float *__restrict__ phi_x,
+                                                                 const void *__restrict__ phi_x,
                                                                  const float *__restrict__ dphi_x,
                                                                  TC *__restrict__ dx, int N, int H) {
     constexpr int LT = prf_ld<TC, M>();
@@ -175,7 +183,16 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
         const long row = bh * N + min(first + kPrfTokensPerBlock * step + pp, N - 1);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            frag_global8(r.ff[s], phi_x + row * M + 32 * s + 8 * g);
+            if constexpr (PH) {  // phi = value plane + remainder plane (bf16 each)
+                const __bf16 *ph = static_cast<const __bf16 *>(phi_x) + row * M + 32 * s + 8 * g;
+                float hv[8], lv[8];
+                unpack16(*reinterpret_cast<const uint4 *>(ph), hv, __bf16());
+                unpack16(*reinterpret_cast<const uint4 *>(ph + (long)gridDim.x * N * M), lv, __bf16());
+#pragma unroll
+                for (int u = 0; u < 8; ++u) r.ff[s].set(u, hv[u] + lv[u]);
+            } else {
+                frag_global8(r.ff[s], static_cast<const float *>(phi_x) + row * M + 32 * s + 8 * g);
+            }
             frag_global8(r.fd[s], dphi_x + row * M + 32 * s + 8 * g);
         }
 #pragma unroll
@@ -221,60 +238,49 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
     }
 }
 
-// bf16 -> fp32 copy of n values (v for the random-feature backward's prefix
-// aggregate), eight per thread and step with 16-byte accesses (both buffers
-// 16-byte aligned); the last n % 8 values one by one.
-__global__ void __launch_bounds__(256) la_convert_kernel(const __bf16 *__restrict__ a, float *__restrict__ b, long n) {
-    const long nv = n / 8;
-    for (long i = blockIdx.x * 256L + threadIdx.x; i < nv; i += (long)gridDim.x * 256L) {
-        float x[8];
-        unpack16(load_stream16(a + 8 * i), x, __bf16());
-        *reinterpret_cast<f32x4 *>(b + 8 * i) = f32x4{x[0], x[1], x[2], x[3]};
-        *reinterpret_cast<f32x4 *>(b + 8 * i + 4) = f32x4{x[4], x[5], x[6], x[7]};
-    }
-    for (long i = 8 * nv + blockIdx.x * 256L + threadIdx.x; i < n; i += (long)gridDim.x * 256L)
-        b[i] = static_cast<float>(a[i]);
-}
-
 template <typename TC, int DK, int M>
 hipError_t launch_prf_t(int what, const void *x, const void *W, const void *f, const void *df, void *out, long BH,
-                        int N, int H, hipStream_t stream) {
+                        int N, int H, hipStream_t stream, void *halves) {
     const int per_wg = kPrfTokensPerBlock * kPrfSteps;
     const dim3 grid((unsigned)BH, (unsigned)((N + per_wg - 1) / per_wg));
     const TC *xc = static_cast<const TC *>(x), *wc = static_cast<const TC *>(W);
     if (what == PRF_VJP)
-        la_prf_vjp_kernel<TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(
-            xc, wc, static_cast<const float *>(f), static_cast<const float *>(df), static_cast<TC *>(out), N, H);
+        la_prf_vjp_kernel<TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, f, static_cast<const float *>(df),
+                                                                        static_cast<TC *>(out), N, H);
+    else if (what == PRF_VJP_PLANES)
+        la_prf_vjp_kernel<TC, DK, M, true><<<grid, kPrfThreads, 0, stream>>>(xc, wc, f, static_cast<const float *>(df),
+                                                                              static_cast<TC *>(out), N, H);
     else if (what == PRF_PHI_F32)
-        la_prf_kernel<TC, float, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<float *>(out), N, H);
+        la_prf_kernel<TC, float, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<float *>(out),
+                                                                          static_cast<__bf16 *>(halves), N, H);
     else
-        la_prf_kernel<TC, TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<TC *>(out), N, H);
+        la_prf_kernel<TC, TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<TC *>(out), nullptr, N, H);
     return hipGetLastError();
 }
 
 template <typename TC, int DK>
 hipError_t launch_prf_dk(int what, const void *x, const void *W, const void *f, const void *df, void *out, long BH,
-                         int N, int H, int M, hipStream_t stream) {
+                         int N, int H, int M, hipStream_t stream, void *halves) {
     switch (M) {
-        case 32: return launch_prf_t<TC, DK, 32>(what, x, W, f, df, out, BH, N, H, stream);
-        case 64: return launch_prf_t<TC, DK, 64>(what, x, W, f, df, out, BH, N, H, stream);
-        case 128: return launch_prf_t<TC, DK, 128>(what, x, W, f, df, out, BH, N, H, stream);
+        case 32: return launch_prf_t<TC, DK, 32>(what, x, W, f, df, out, BH, N, H, stream, halves);
+        case 64: return launch_prf_t<TC, DK, 64>(what, x, W, f, df, out, BH, N, H, stream, halves);
+        case 128: return launch_prf_t<TC, DK, 128>(what, x, W, f, df, out, BH, N, H, stream, halves);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_prf_any(bool bf16, int what, const void *x, const void *W, const void *f, const void *df,
-                          void *out, long BH, int N, int H, int DK, int M, hipStream_t stream) {
+                          void *out, long BH, int N, int H, int DK, int M, hipStream_t stream, void *halves) {
     switch (DK) {
         case 32:
-            return bf16 ? launch_prf_dk<__bf16, 32>(what, x, W, f, df, out, BH, N, H, M, stream)
-                        : launch_prf_dk<float, 32>(what, x, W, f, df, out, BH, N, H, M, stream);
+            return bf16 ? launch_prf_dk<__bf16, 32>(what, x, W, f, df, out, BH, N, H, M, stream, halves)
+                        : launch_prf_dk<float, 32>(what, x, W, f, df, out, BH, N, H, M, stream, halves);
         case 64:
-            return bf16 ? launch_prf_dk<__bf16, 64>(what, x, W, f, df, out, BH, N, H, M, stream)
-                        : launch_prf_dk<float, 64>(what, x, W, f, df, out, BH, N, H, M, stream);
+            return bf16 ? launch_prf_dk<__bf16, 64>(what, x, W, f, df, out, BH, N, H, M, stream, halves)
+                        : launch_prf_dk<float, 64>(what, x, W, f, df, out, BH, N, H, M, stream, halves);
         case 128:
-            return bf16 ? launch_prf_dk<__bf16, 128>(what, x, W, f, df, out, BH, N, H, M, stream)
-                        : launch_prf_dk<float, 128>(what, x, W, f, df, out, BH, N, H, M, stream);
+            return bf16 ? launch_prf_dk<__bf16, 128>(what, x, W, f, df, out, BH, N, H, M, stream, halves)
+                        : launch_prf_dk<float, 128>(what, x, W, f, df, out, BH, N, H, M, stream, halves);
         default: return hipErrorInvalidValue;
     }
 }
@@ -282,18 +288,10 @@ hipError_t launch_prf_any(bool bf16, int what, const void *x, const void *W, con
 }  // namespace
 
 hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const void *f, const void *df, void *out,
-                      long BH, int N, int H, int DK, int M, hipStream_t stream) {
-    return launch_prf_any(bf16, what, x, W, f, df, out, BH, N, H, DK, M, stream);
+                      long BH, int N, int H, int DK, int M, hipStream_t stream, void *halves) {
+    return launch_prf_any(bf16, what, x, W, f, df, out, BH, N, H, DK, M, stream, halves);
 }
 
-hipError_t launch_convert(const void *a, void *b, long n, hipStream_t stream) {
-    if (n <= 0) return hipSuccess;
-    long blocks = (n / 8 + 255) / 256;  // eight values per thread
-    if (blocks < 1) blocks = 1;
-    if (blocks > 8192) blocks = 8192;
-    la_convert_kernel<<<(unsigned)blocks, 256, 0, stream>>>(static_cast<const __bf16 *>(a), static_cast<float *>(b), n);
-    return hipGetLastError();
-}
 
 }  // namespace la
 
@@ -307,13 +305,15 @@ bool prf_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of the random map.  Forward: phi(q), phi(k) as [BH][N][m] in the
-// input type, then the inner call's workspace.  Backward: phi(q), phi(k),
-// dphi(q), dphi(k) in fp32 and, for bf16 inputs, an fp32 copy of v (for the
-// prefix aggregate), then the inner backward's workspace.
+// input type, then the inner call's workspace.  Backward: phi(q), phi(k) in
+// fp32 (bf16 inputs: as two bf16 planes each, value and remainder, the same
+// bytes), dphi(q), dphi(k) in fp32, for bf16 inputs the segment sums of the
+// prefix aggregate's remainder pass, then the inner backward's workspace.
 struct FmLayout {
-    size_t fq, fk, dfq, dfk, v32, inner, total;
+    size_t fq, fk, dfq, dfk, agglo, inner, total;
 };
-FmLayout fm_layout(bool bwd, int B, int H, int N, int m, int d_v, int in, size_t inner_bytes) {
+// (C: the backward's chunk size, which sizes the prefix aggregate's slots.)
+FmLayout fm_layout(bool bwd, int B, int H, int N, int m, int d_v, int C, int in, size_t inner_bytes) {
     const size_t th = (size_t)B * H * N;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -328,7 +328,11 @@ FmLayout fm_layout(bool bwd, int B, int H, int N, int m, int d_v, int in, size_t
     if (bwd) {
         l.dfq = take(th * m * 4);
         l.dfk = take(th * m * 4);
-        if (in == LA_BF16) l.v32 = take(th * d_v * 4);
+        if (in == LA_BF16) {
+            int L = 0;
+            const long Pmax = la::plan_segments((long)B * H, N, C, la::kMaxTargetWg, &L);
+            l.agglo = take((size_t)B * H * Pmax * ((size_t)m * d_v + m) * 4);
+        }
     }
     l.inner = off;
     l.total = off + inner_bytes;
@@ -369,7 +373,7 @@ size_t la_fwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, i
     if (fm != LA_PHI_PRF) return inner;
     if (B < 1 || H < 1 || N < 1 || N > la::kMaxN || !la::dim_ok(d_v) || !la::chunk_ok(C) || !la::dtype_ok(in)) return 0;
     if (prf_fused(in, d_k, m, d_v, C)) return inner;
-    return fm_layout(false, B, H, N, m, d_v, in, inner).total;
+    return fm_layout(false, B, H, N, m, d_v, 0, in, inner).total;
 }
 
 size_t la_fwd_noncausal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, la_feature_map fm, int m,
@@ -380,7 +384,7 @@ size_t la_fwd_noncausal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v
     if (fm != LA_PHI_PRF) return inner;
     if (inner == 0 || !la::dtype_ok(in)) return 0;
     if (prf_fused(in, d_k, m, d_v, la::kNonCausalChunk)) return inner;
-    return fm_layout(false, B, H, N, m, d_v, in, inner).total;
+    return fm_layout(false, B, H, N, m, d_v, 0, in, inner).total;
 }
 
 size_t la_bwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, int C, la_feature_map fm, int m,
@@ -391,7 +395,7 @@ size_t la_bwd_causal_fm_workspace_bytes(int B, int H, int N, int d_k, int d_v, i
     const size_t inner = la::bwd_workspace_bytes(B, H, N, mf, d_v, C);
     if (fm != LA_PHI_PRF) return inner;
     if (!la::dtype_ok(in)) return 0;
-    return fm_layout(true, B, H, N, m, d_v, in, inner).total;
+    return fm_layout(true, B, H, N, m, d_v, C, in, inner).total;
 }
 
 la_status la_fwd_causal_fm(const void *q, const void *k, const void *v, void *o, float *den, la_feature_map fm,
@@ -412,7 +416,7 @@ la_status la_fwd_causal_fm(const void *q, const void *k, const void *v, void *o,
         d.phi_id = la::kPhiPrfFused;
         d.W = W;
     } else if (fm == LA_PHI_PRF) {
-        const FmLayout l = fm_layout(false, B, H, N, m, d_v, in, 0);
+        const FmLayout l = fm_layout(false, B, H, N, m, d_v, 0, in, 0);
         const long BH = (long)B * H;
         hipError_t e = la::launch_prf(in == LA_BF16, la::PRF_PHI, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k,
                                       m, stream);
@@ -447,7 +451,7 @@ la_status la_fwd_noncausal_fm(const void *q, const void *k, const void *v, void 
         d.phi_id = la::kPhiPrfFused;
         d.W = W;
     } else if (fm == LA_PHI_PRF) {
-        const FmLayout l = fm_layout(false, B, H, N, m, d_v, in, 0);
+        const FmLayout l = fm_layout(false, B, H, N, m, d_v, 0, in, 0);
         const long BH = (long)B * H;
         hipError_t e = la::launch_prf(in == LA_BF16, la::PRF_PHI, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k,
                                       m, stream);
@@ -480,19 +484,22 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     if (fm == LA_PHI_ELU1) return la_bwd_causal(q, k, v, dO, dq, dk, dv, B, H, N, d_k, d_v, C, in, ws, ws_bytes, stream);
     la::BwdDesc d{q, k, v, dO, dq, dk, dv, B, H, N, mf, d_v, C, in == LA_BF16, static_cast<float *>(ws), stream, 0, 1};
     if (fm == LA_PHI_IDENTITY) return la::from_hip(la::run_bwd(d));
-    // Random features: the sweeps read fp32 features and write dphi in fp32,
+    // Random features: the sweeps read the features and write dphi in fp32,
     // so that the chain rule gets it far more accurate than a bf16 rounding of
-    // the features would leave it.  fp32 inputs: fp32 products.  bf16 inputs:
-    // products of bf16 value-plus-remainder pairs (about 16 bits, four bf16
-    // MFMAs each) on the bf16 v and dO as given, dv written in bf16; only the
-    // prefix aggregate, whose products stay fp32, reads an fp32 copy of v.
-    const FmLayout l = fm_layout(true, B, H, N, m, d_v, in, 0);
+    // the features would leave it.  fp32 inputs: fp32 features and products.
+    // bf16 inputs: features as a bf16 value and a bf16 remainder (two planes,
+    // about 16 bits), products of such pairs (four bf16 MFMAs each) on the
+    // bf16 v and dO as given, dv written in bf16, and the prefix aggregate as
+    // two bf16 passes, one per plane of phi(k).
+    const FmLayout l = fm_layout(true, B, H, N, m, d_v, C, in, 0);
     const long BH = (long)B * H;
     const bool bf = in == LA_BF16;
-    hipError_t e = la::launch_prf(bf, la::PRF_PHI_F32, q, W, nullptr, nullptr, at(ws, l.fq), BH, N, H, d_k, m, stream);
-    if (e == hipSuccess)
-        e = la::launch_prf(bf, la::PRF_PHI_F32, k, W, nullptr, nullptr, at(ws, l.fk), BH, N, H, d_k, m, stream);
-    if (e == hipSuccess && bf) e = la::launch_convert(v, at(ws, l.v32), BH * N * (long)d_v, stream);
+    hipError_t e = hipSuccess;
+    for (int t = 0; t < 2 && e == hipSuccess; ++t) {
+        void *fx = at(ws, t == 0 ? l.fq : l.fk);
+        e = la::launch_prf(bf, la::PRF_PHI_F32, t == 0 ? q : k, W, nullptr, nullptr, bf ? nullptr : fx, BH, N, H,
+                           d_k, m, stream, bf ? fx : nullptr);
+    }
     if (e != hipSuccess) return la::from_hip(e);
     d.q = at(ws, l.fq);
     d.k = at(ws, l.fk);
@@ -501,13 +508,13 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     d.in_bf16 = 0;
     if (bf) {
         d.pair_ops = 1;
-        d.v_agg = at(ws, l.v32);
+        d.agg_lo = reinterpret_cast<float *>(at(ws, l.agglo));
     }
     d.ws = reinterpret_cast<float *>(at(ws, l.inner));
     if ((e = la::run_bwd(d)) != hipSuccess) return la::from_hip(e);
-    e = la::launch_prf(bf, la::PRF_VJP, q, W, at(ws, l.fq), at(ws, l.dfq), dq, BH, N, H, d_k, m, stream);
-    if (e == hipSuccess)
-        e = la::launch_prf(bf, la::PRF_VJP, k, W, at(ws, l.fk), at(ws, l.dfk), dk, BH, N, H, d_k, m, stream);
+    const int vjp = bf ? la::PRF_VJP_PLANES : la::PRF_VJP;
+    e = la::launch_prf(bf, vjp, q, W, at(ws, l.fq), at(ws, l.dfq), dq, BH, N, H, d_k, m, stream);
+    if (e == hipSuccess) e = la::launch_prf(bf, vjp, k, W, at(ws, l.fk), at(ws, l.dfk), dk, BH, N, H, d_k, m, stream);
     return la::from_hip(e);
 }
 

@@ -26,14 +26,16 @@ namespace la {
 // s - 1.  Mode 2: an aggregate is normalised at its segment's first token, so
 // the suffix after segment s is the aggregate of s + 1 plus gamma^L times the
 // suffix after s + 1.
+// add (mode 0): aggregates in ws's layout added to ws's as they are read.
 static __global__ void __launch_bounds__(256)
 la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, int DV, int mode, int lim,
-                   const float *gamma, int H, int L) {
+                   const float *gamma, int H, int L, const float *add) {
     const int SS = DK * DV + DK;
     const long bh = blockIdx.x;
     const int idx = blockIdx.y * 256 + threadIdx.x;
     if (idx >= SS) return;
     float *base = ws + bh * (long)P * SS + idx;
+    const float *abase = add ? add + bh * (long)P * SS + idx : nullptr;
     float f = 1.0f;  // gamma^L by repeated squaring
     if (gamma) {
         float b = gamma[bh % H];
@@ -50,7 +52,7 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
             run = z0[bh * (long)DK + (idx - DK * DV)];
         }
         for (int s = 0; s < lim; ++s) {
-            const float a = base[(long)s * SS];
+            const float a = base[(long)s * SS] + (abase ? abase[(long)s * SS] : 0.0f);
             base[(long)s * SS] = run;
             run = f * run + a;
         }
@@ -71,11 +73,12 @@ la_seg_scan_kernel(float *ws, const float *S0, const float *z0, int P, int DK, i
 }
 
 hipError_t launch_seg_scan(float *ws, const float *S0, const float *z0, long BH, int P, int DK, int DV,
-                           int mode, int lim, hipStream_t stream, const float *gamma, int H, int L) {
-    if (lim < 0 || lim > P) return hipErrorInvalidValue;
+                           int mode, int lim, hipStream_t stream, const float *gamma, int H, int L,
+                           const float *add) {
+    if (lim < 0 || lim > P || (add && mode != 0)) return hipErrorInvalidValue;
     const long SS = state_floats(DK, DV);
     const dim3 grid((unsigned)BH, (unsigned)((SS + 255) / 256));
-    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode, lim, gamma, H, L);
+    la_seg_scan_kernel<<<grid, 256, 0, stream>>>(ws, S0, z0, P, DK, DV, mode, lim, gamma, H, L, add);
     return hipGetLastError();
 }
 
