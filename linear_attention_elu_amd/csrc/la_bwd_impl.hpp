@@ -172,8 +172,8 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
 
     // Rows [0, CM) of the tile (leading dimension LD) from the registers; zero
     // past nrows (FULL: the caller knows nrows == CM).  bf16-pair tiles take
-    // loaded fp32 words as value-plus-remainder words, and loaded bf16 values
-    // as pair words with a zero remainder (eight words from each vector).
+    // loaded fp32 words, or a value plane and a remainder plane, as
+    // value-plus-remainder words.
     template <int LD, bool FULL, typename TT>
     __device__ __forceinline__ void store(TT *tile, int nrows, int tid) const {
 #pragma unroll
@@ -183,11 +183,7 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
             uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
-            if constexpr (std::is_same<TT, bf16p>::value && std::is_same<TI, __bf16>::value) {
-                uint4 *dst = reinterpret_cast<uint4 *>(tile + row * LD + col);
-                dst[0] = make_uint4(w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16);
-                dst[1] = make_uint4(w.z & 0xffffu, w.z >> 16, w.w & 0xffffu, w.w >> 16);
-            } else if constexpr (HALVES) {
+            if constexpr (HALVES) {
                 static_assert(std::is_same<TT, bf16p>::value, "bf16 planes stage into pair tiles");
                 // pair word = value half | remainder half << 16, element by element
                 const uint4 l = (FULL || row < nrows) ? ul[it] : make_uint4(0, 0, 0, 0);
@@ -197,7 +193,7 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
                 dst[1] = make_uint4(__builtin_amdgcn_perm(l.z, w.z, 0x05040100u), __builtin_amdgcn_perm(l.z, w.z, 0x07060302u),
                                     __builtin_amdgcn_perm(l.w, w.w, 0x05040100u), __builtin_amdgcn_perm(l.w, w.w, 0x07060302u));
             } else {
-                static_assert(std::is_same<TT, TI>::value, "staging: tile of the loaded type, or bf16 into pairs");
+                static_assert(std::is_same<TT, TI>::value, "staging: tile of the loaded type, or planes into pairs");
                 if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
                 *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
             }
@@ -221,18 +217,25 @@ __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
 // r_seg = sum_i (phi(q_i) a_i) e_i over the segment (token p of the segment
 // weighs gamma^p with a decay), so no separate pass re-reads q and dO.
 // ---------------------------------------------------------------------------
+// Tile type of v and dO: with bf16-pair sweeps they stay bf16 tiles (the
+// values are bf16 exactly), and their fragments meet pairs in two-MFMA
+// products; otherwise the input type.
+template <typename TI>
+using bwd_tv = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
+
 template <int DK, int DV, typename TI, bool DEC = false> struct DqSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
     static constexpr int LK = BwdLd<TI, DK>::TR;   // phi(K): transpose reads
     static constexpr int LQ = BwdLd<TI, DK>::ROW;  // phi(Q): row reads
-    static constexpr int LV = BwdLd<TI, DV>::TR;   // V: transpose reads (state), row reads (M)
-    static constexpr int LG = BwdLd<TI, DV>::ROW;  // dO: row reads
+    using TV = bwd_tv<TI>;
+    static constexpr int LV = BwdLd<TV, DV>::TR;   // V: transpose reads (state), row reads (M)
+    static constexpr int LG = BwdLd<TV, DV>::ROW;  // dO: row reads
     static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[i][j]
     static constexpr bool LO = sizeof(TI) == 2;     // M kept as value + remainder
     alignas(16) TI k[CM * LK];
     alignas(16) TI q[CM * LQ];
-    alignas(16) TI v[CM * LV];
-    alignas(16) TI g[CM * LG];
+    alignas(16) TV v[CM * LV];
+    alignas(16) TV g[CM * LG];
     alignas(16) TI mh[CM * LM];
     alignas(16) TI ml[LO ? CM * LM : 4];
     alignas(16) float red[kBwdWaves][CM][2];  // per-wave partial phi(q).X and phi(q).z
@@ -245,6 +248,7 @@ template <int DK, int DV, typename TI, bool NC = false, bool DECAY = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dq_kernel(const BwdParams p) {
     using TC = TI;
+    using TV = bwd_tv<TI>;  // v and dO tiles and fragments
     constexpr bool dec = DECAY && !NC;
     using SM = DqSmem<DK, DV, TI, dec>;
     constexpr int NW = kBwdWaves;
@@ -323,16 +327,14 @@ la_bwd_dq_kernel(const BwdParams p) {
         }
     };
     refresh();
-    Frag<TC> ones;
+    Frag<TV> ones;
     frag_ones(ones);
 
     // q, k: two bf16 planes (value, remainder) for bf16-pair sweeps
     using TQ = typename std::conditional<std::is_same<TI, bf16p>::value, bf16h, TI>::type;
     const long fplane = (long)gridDim.x * N * DK;  // elements per plane
     RowRegs<TQ, DK, kBwdThreads, SM::CM> xk, xq;
-    // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
-    using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
-    RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
+    RowRegs<TV, DV, kBwdThreads, SM::CM> xv, xg;
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
         const int nrows = min(C, row_end - r0);
@@ -348,8 +350,8 @@ la_bwd_dq_kernel(const BwdParams p) {
     }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
-    const lds_vptr<TC> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
-    const lds_vptr<TC> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
+    const lds_vptr<TV> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
+    const lds_vptr<TV> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
     const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 16 * eb + 4 * g);
     const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
     const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
@@ -383,7 +385,7 @@ la_bwd_dq_kernel(const BwdParams p) {
             f32x4 acc = zero4;
 #pragma unroll
             for (int s = 0; s < NSV; ++s) {
-                Frag<TC> fv, fg;
+                Frag<TV> fv, fg;
                 lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
                 lds_frag_split_v(fg, gb, 16 * I * SM::LG + 32 * s);
                 acc = mma(fv, fg, acc);
@@ -413,7 +415,7 @@ la_bwd_dq_kernel(const BwdParams p) {
                 X[I] = zero4;
                 Z[I] = zero4;
                 if (I < nib) {
-                    Frag<TC> fg[NSV];
+                    Frag<TV> fg[NSV];
 #pragma unroll
                     for (int s = 0; s < NSV; ++s) lds_frag_split_v(fg[s], gb, 16 * I * SM::LG + 32 * s);
                     f32x4 ax = zero4, az = accZ;
@@ -430,7 +432,8 @@ la_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
                     for (int jp = 0; jp < NTS; ++jp) {
                         if (!NC && 2 * jp <= I) {
-                            Frag<TC> fm, ftr;
+                            Frag<TC> fm;
+                            Frag<TV> ftr;
                             lds_frag_split_v(fm, mhb, 16 * I * SM::LM + 32 * jp);
                             ax = mma(fkt[jp], fm, ax);
                             if constexpr (SM::LO) {
@@ -548,7 +551,7 @@ la_bwd_dq_kernel(const BwdParams p) {
                         if constexpr (SM::LO) accrs = mma(fq, fe_lo, accrs);
 #pragma unroll
                         for (int cv = 0; cv < CV; ++cv) {
-                            Frag<TC> fgc;
+                            Frag<TV> fgc;
                             lds_frag_tr(fgc, sm.g, SM::LG, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
                             accRs[cv] = mma(fgc, fq, accRs[cv]);
                         }
@@ -587,7 +590,7 @@ la_bwd_dq_kernel(const BwdParams p) {
                 if constexpr (dec && SLO) accZ = mma(fkl, ones, accZ);
 #pragma unroll
                 for (int cv = 0; cv < CV; ++cv) {
-                    Frag<TC> fvt;
+                    Frag<TV> fvt;
                     lds_frag_tr(fvt, sm.v, SM::LV, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
                     accS[cv] = mma(fvt, fkt[s], accS[cv]);
                     if constexpr (dec && SLO) accS[cv] = mma(fvt, fkl, accS[cv]);
@@ -618,16 +621,17 @@ template <int DK, int DV, typename TI> struct DkvSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
     static constexpr int LQ = BwdLd<TI, DK>::TR;   // phi(Q): transpose reads (dk, state), row reads (A)
     static constexpr int LK = BwdLd<TI, DK>::ROW;  // phi(K): row reads
-    static constexpr int LV = BwdLd<TI, DV>::ROW;  // V: row reads
-    static constexpr int LG = BwdLd<TI, DV>::TR;   // dO: transpose reads (dv, state), row reads (M)
+    using TV = bwd_tv<TI>;
+    static constexpr int LV = BwdLd<TV, DV>::ROW;  // V: row reads
+    static constexpr int LG = BwdLd<TV, DV>::TR;   // dO: transpose reads (dv, state), row reads (M)
     static constexpr int LR = BwdLd<TI, DV>::TR;   // R[e][c']: transpose reads
     static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[j][i], A[j][i]
     static constexpr int RROWS = DK < 32 ? 32 : DK;
     static constexpr bool LO = sizeof(TI) == 2;
     alignas(16) TI q[CM * LQ];
     alignas(16) TI k[CM * LK];
-    alignas(16) TI v[CM * LV];
-    alignas(16) TI g[CM * LG];
+    alignas(16) TV v[CM * LV];
+    alignas(16) TV g[CM * LG];
     alignas(16) TI R[RROWS * LR];  // copy of the suffix state R[e][c'] for the dv product
     alignas(16) TI mh[CM * LM];
     alignas(16) TI ml[LO ? CM * LM : 4];
@@ -640,6 +644,7 @@ template <int DK, int DV, typename TI, bool NC = false, bool DECAY = false>
 __global__ void __launch_bounds__(kBwdThreads)
 la_bwd_dkdv_kernel(const BwdParams p) {
     using TC = TI;
+    using TV = bwd_tv<TI>;  // v and dO tiles and fragments
     constexpr bool dec = DECAY && !NC;
     using SM = DkvSmem<DK, DV, TI>;
     constexpr int NW = kBwdWaves;
@@ -710,9 +715,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     using TQ = typename std::conditional<std::is_same<TI, bf16p>::value, bf16h, TI>::type;
     const long fplane = (long)gridDim.x * N * DK;  // elements per plane
     RowRegs<TQ, DK, kBwdThreads, SM::CM> xq, xk;
-    // v and dO: bf16 in memory for bf16-pair sweeps, staged into pair tiles
-    using TG = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
-    RowRegs<TG, DV, kBwdThreads, SM::CM> xv, xg;
+    RowRegs<TV, DV, kBwdThreads, SM::CM> xv, xg;
     float xe = 0.f, xa = 0.f;  // e and a of token tid (tid < CM)
     auto fetch = [&](int ch) {
         const int r0 = row_begin + ch * C;
@@ -736,8 +739,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     // per-lane bases of the row-wise reads: row pp, column 4g
     const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 4 * g);
     const lds_vptr<TC> kb = lds_v(sm.k + pp * SM::LK + 4 * g);
-    const lds_vptr<TC> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
-    const lds_vptr<TC> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
+    const lds_vptr<TV> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
+    const lds_vptr<TV> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
     const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
     const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
     const lds_vptr<TC> atb = lds_v(sm.at + pp * SM::LM + 4 * g);
@@ -777,7 +780,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
             if (!is_a) {
 #pragma unroll
                 for (int s = 0; s < NSV; ++s) {
-                    Frag<TC> fg, fv;
+                    Frag<TV> fg, fv;
                     lds_frag_split_v(fg, gb, 16 * I * SM::LG + 32 * s);
                     lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
                     acc = mma(fg, fv, acc);
@@ -819,7 +822,8 @@ la_bwd_dkdv_kernel(const BwdParams p) {
         }
         __syncthreads();  // M and A blocks are in LDS; R copy reads done
 
-        Frag<TC> fqt[NTS], fgt[NTS];  // phi(Q) (features 16 eb + pp), dO (values 16 cb + pp) over queries
+        Frag<TC> fqt[NTS];  // phi(Q) (features 16 eb + pp) over queries
+        Frag<TV> fgt[NTS];  // dO (values 16 cb + pp) over queries
         if (has_e && !NC) {
 #pragma unroll
             for (int ip = 0; ip < NTS; ++ip)
@@ -843,7 +847,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     if constexpr (dec) {
 #pragma unroll
                         for (int s = 0; s < NSV; ++s) {
-                            Frag<TC> fv;
+                            Frag<TV> fv;
                             lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
                             acc = mma(fragR[s], fv, acc);
                             if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
@@ -865,7 +869,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     if constexpr (!dec) {
 #pragma unroll
                         for (int s = 0; s < NSV; ++s) {
-                            Frag<TC> fv;
+                            Frag<TV> fv;
                             lds_frag_split_v(fv, vb, 16 * J * SM::LV + 32 * s);
                             acc = mma(fragR[s], fv, acc);
                             if constexpr (RLO) acc = mma(fragR_lo[s], fv, acc);
@@ -907,7 +911,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                             acc = mma(frt[s], fk, acc);
                         }
                     }
-                    if (valid) store4<TG>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
+                    if (valid) store4<TV>(p.dv, orow * DV + 16 * cb + 4 * g, acc);
                 }
             }
         }
@@ -949,7 +953,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     if constexpr (SM::LO) accr = mma(fq, fe_lo, accr);
 #pragma unroll
                     for (int cv = 0; cv < CV; ++cv) {
-                        Frag<TC> fgc;
+                        Frag<TV> fgc;
                         lds_frag_tr(fgc, sm.g, SM::LG, 32 * s + 4 * g, 32 * s + 16 + 4 * g, 16 * cv, pp);
                         accR[cv] = mma(fgc, fq, accR[cv]);
                     }

@@ -158,6 +158,17 @@ __device__ __forceinline__ f32x4 mma(const Frag<bf16p> &a, const Frag<bf16p> &b,
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, c, 0, 0, 0);
 }
 
+// A pair with a bf16 operand (a value a bf16 holds exactly): two MFMAs, each
+// product of halves exact in fp32 as above.
+__device__ __forceinline__ f32x4 mma(const Frag<bf16p> &a, const Frag<__bf16> &b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.v, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<__bf16> &a, const Frag<bf16p> &b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.lo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.hi, c, 0, 0, 0);
+}
+
 // Eight pair words (slots 0..7) to a fragment: the value halves of two words
 // side by side form one bf16 pair of the hi vector, the remainder halves one
 // of the lo vector (v_perm byte selects).
