@@ -122,9 +122,9 @@ constexpr int kNonCausalChunk = 64;
 // The random-feature map and its backward (la_prf.hip), x [BH][N][DK] and the
 // directions W [H][M][DK] in the input type:
 //   PRF_PHI      out = phi(x) [BH][N][M] in the input type;
-//   PRF_PHI_F32  out = phi(x) in fp32 (out may be null), and with halves
-//                non-null phi(x) as its bf16 value (plane 0) and bf16
-//                remainder (plane 1), bf16 [2][BH][N][M];
+//   PRF_PHI_F32  out = phi(x) in fp32, or with halves non-null phi(x) as
+//                its bf16 value (plane 0) and bf16 remainder (plane 1) at
+//                halves, bf16 [2][BH][N][M] (out unused);
 //   PRF_VJP      out = dx [BH][N][DK] (input type) from x, f = phi(x) and
 //                df = dphi, both fp32;
 //   PRF_VJP_PLANES  the same with f = phi(x) as the two bf16 planes.

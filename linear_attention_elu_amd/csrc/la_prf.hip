@@ -91,13 +91,19 @@ template <typename TC> __device__ __forceinline__ f32x4 load4(const TC *p) {
 // kPrfSteps blocks 64 tokens apart with two register sets: the rows of block
 // i + 1 are in flight while block i is computed, and those of block 0 are
 // issued before W is staged.
-template <typename TC, typename TO, int DK, int M>
+// HV: phi goes out as two bf16 planes (value, remainder) at halves instead
+// of to out.  A lane's four features of one token are 16 apart from one
+// feature tile to the next, so the wave first gathers its 16 tokens' rows in
+// LDS and then writes whole 16-byte pieces of each row.
+template <typename TC, typename TO, int DK, int M, bool HV = false>
 __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
                                                              TO *__restrict__ out, __bf16 *__restrict__ halves, int N,
                                                              int H) {
     constexpr int LW = prf_ld<TC, DK>();
     constexpr int NF = M / 16, NS = DK / 32;
+    constexpr int LR = M + 8;  // row of the gather tile (bf16), 16-byte aligned, banks staggered
     __shared__ __attribute__((aligned(16))) TC sw[M * LW];
+    __shared__ __attribute__((aligned(16))) __bf16 srow[HV ? (kPrfThreads / 64) * 2 * 16 * LR : 8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, pp = lane & 15;
     const long bh = blockIdx.x;
     const int first = blockIdx.y * (kPrfSteps * kPrfTokensPerBlock) + 16 * wave;  // this wave's block 0
@@ -134,21 +140,44 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
             }
         }
         nx = sum_over_groups(nx);
-        if (t0 + pp < N) {
+        if constexpr (HV) {
+            // rows of this wave's 16 tokens: plane 0 the bf16 value, plane 1 the bf16 remainder
+            __bf16 *rows = srow + wave * (2 * 16 * LR);
 #pragma unroll
             for (int F = 0; F < NF; ++F) {
                 f32x4 f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) f[r] = __expf(acc[F][r] - 0.5f * nx) * scale;
-                if (out) store4_to(out + (bh * N + t0 + pp) * (long)M + 16 * F + 4 * g, f);  // uniform
-                if (halves) {  // uniform: phi as its bf16 value and bf16 remainder, two planes
-                    const long at = (bh * N + t0 + pp) * (long)M + 16 * F + 4 * g;
-                    const uint2 hv = pack_bf16x4(f);
-                    const f32x4 h = {__uint_as_float(hv.x << 16), __uint_as_float(hv.x & 0xffff0000u),
-                                     __uint_as_float(hv.y << 16), __uint_as_float(hv.y & 0xffff0000u)};
-                    *reinterpret_cast<uint2 *>(halves + at) = hv;
-                    *reinterpret_cast<uint2 *>(halves + (long)gridDim.x * N * M + at) = pack_bf16x4(f - h);
-                }
+                const uint2 hv = pack_bf16x4(f);
+                const f32x4 h = {__uint_as_float(hv.x << 16), __uint_as_float(hv.x & 0xffff0000u),
+                                 __uint_as_float(hv.y << 16), __uint_as_float(hv.y & 0xffff0000u)};
+                *reinterpret_cast<uint2 *>(rows + pp * LR + 16 * F + 4 * g) = hv;
+                *reinterpret_cast<uint2 *>(rows + (16 + pp) * LR + 16 * F + 4 * g) = pack_bf16x4(f - h);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // 16-byte pieces: M / 8 per row, 16 rows per plane
+            constexpr int PR = M / 8;
+#pragma unroll
+            for (int c = lane; c < 2 * 16 * PR; c += 64) {
+                const int plane = c / (16 * PR), tok = (c / PR) % 16, col = 8 * (c % PR);
+                const uint4 piece = *reinterpret_cast<const uint4 *>(rows + (16 * plane + tok) * LR + col);
+                if (t0 + tok < N)
+                    *reinterpret_cast<uint4 *>(halves + plane * (long)gridDim.x * N * M + (bh * N + t0 + tok) * (long)M +
+                                               col) = piece;
+            }
+            // the next step's rows overwrite these only after every lane has read them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        } else if (t0 + pp < N) {
+#pragma unroll
+            for (int F = 0; F < NF; ++F) {
+                f32x4 f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f[r] = __expf(acc[F][r] - 0.5f * nx) * scale;
+                store4_to(out + (bh * N + t0 + pp) * (long)M + 16 * F + 4 * g, f);
             }
         }
     }
@@ -250,9 +279,12 @@ hipError_t launch_prf_t(int what, const void *x, const void *W, const void *f, c
     else if (what == PRF_VJP_PLANES)
         la_prf_vjp_kernel<TC, DK, M, true><<<grid, kPrfThreads, 0, stream>>>(xc, wc, f, static_cast<const float *>(df),
                                                                               static_cast<TC *>(out), N, H);
+    else if (what == PRF_PHI_F32 && halves)
+        la_prf_kernel<TC, float, DK, M, true><<<grid, kPrfThreads, 0, stream>>>(xc, wc, nullptr,
+                                                                                static_cast<__bf16 *>(halves), N, H);
     else if (what == PRF_PHI_F32)
-        la_prf_kernel<TC, float, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<float *>(out),
-                                                                          static_cast<__bf16 *>(halves), N, H);
+        la_prf_kernel<TC, float, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<float *>(out), nullptr,
+                                                                          N, H);
     else
         la_prf_kernel<TC, TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, static_cast<TC *>(out), nullptr, N, H);
     return hipGetLastError();
