@@ -102,7 +102,8 @@ struct Decay {
 };
 
 template <typename TI, int DK, int DV> constexpr int bwd_cmax() {
-    return (sizeof(TI) == 4 && (DK > 64 || DV > 64)) ? 32 : 64;
+    // fp32 and bf16-pair tiles take twice the bf16 bytes
+    return ((sizeof(TI) == 4 || std::is_same<TI, bf16p>::value) && (DK > 64 || DV > 64)) ? 32 : 64;
 }
 
 // Leading dimensions (elements) of a tile of D columns (padded to >= 32).
@@ -124,6 +125,13 @@ __device__ __forceinline__ void lower_block(int b, int &I, int &J) {
 // chunk c is computed.  Every lane issues the same number of loads (rows past
 // the chunk's end are clamped to its last row and zeroed at the store), which
 // keeps the wait before the store exact.
+template <typename T> struct plane_of {
+    static constexpr int value = 0;
+};
+template <int PL> struct plane_of<bf16pl<PL>> {
+    static constexpr int value = PL;
+};
+
 template <typename TI, int D, int NT, int CM> struct RowRegs {
     static constexpr bool HALVES = std::is_same<TI, bf16h>::value;  // two bf16 planes, `plane` elements apart
     static constexpr int VEC = Store<TI>::VEC;
@@ -171,9 +179,8 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
     }
 
     // Rows [0, CM) of the tile (leading dimension LD) from the registers; zero
-    // past nrows (FULL: the caller knows nrows == CM).  bf16-pair tiles take
-    // loaded fp32 words, or a value plane and a remainder plane, as
-    // value-plus-remainder words.
+    // past nrows (FULL: the caller knows nrows == CM).  Loaded value and
+    // remainder planes go to the two planes of a pair tile.
     template <int LD, bool FULL, typename TT>
     __device__ __forceinline__ void store(TT *tile, int nrows, int tid) const {
 #pragma unroll
@@ -183,27 +190,22 @@ template <typename TI, int D, int NT, int CM> struct RowRegs {
             const int row = idx / VPR;
             const int col = (idx % VPR) * VEC;
             uint4 w = (FULL || row < nrows) ? u[it] : make_uint4(0, 0, 0, 0);
-            if constexpr (HALVES) {
-                static_assert(std::is_same<TT, bf16p>::value, "bf16 planes stage into pair tiles");
-                // pair word = value half | remainder half << 16, element by element
+            if constexpr (HALVES) {  // value plane and remainder plane into the tile's two planes
                 const uint4 l = (FULL || row < nrows) ? ul[it] : make_uint4(0, 0, 0, 0);
-                uint4 *dst = reinterpret_cast<uint4 *>(tile + row * LD + col);
-                dst[0] = make_uint4(__builtin_amdgcn_perm(l.x, w.x, 0x05040100u), __builtin_amdgcn_perm(l.x, w.x, 0x07060302u),
-                                    __builtin_amdgcn_perm(l.y, w.y, 0x05040100u), __builtin_amdgcn_perm(l.y, w.y, 0x07060302u));
-                dst[1] = make_uint4(__builtin_amdgcn_perm(l.z, w.z, 0x05040100u), __builtin_amdgcn_perm(l.z, w.z, 0x07060302u),
-                                    __builtin_amdgcn_perm(l.w, w.w, 0x05040100u), __builtin_amdgcn_perm(l.w, w.w, 0x07060302u));
+                *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
+                *reinterpret_cast<uint4 *>(tile + row * LD + col + plane_of<TT>::value) = l;
             } else {
                 static_assert(std::is_same<TT, TI>::value, "staging: tile of the loaded type, or planes into pairs");
-                if constexpr (std::is_same<TI, bf16p>::value) w = bf16p_pack4(w);
                 *reinterpret_cast<uint4 *>(tile + row * LD + col) = w;
             }
         }
     }
 };
 
+// (TI = bf16p, the pair sweeps: fp32 outputs, as for TI = float.)
 template <typename TI>
 __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
-    if constexpr (sizeof(TI) == 2) {
+    if constexpr (std::is_same<TI, __bf16>::value) {
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + idx) = pack_bf16x4(a);
     } else {
         *reinterpret_cast<f32x4 *>(static_cast<float *>(dst) + idx) = a;
@@ -217,27 +219,35 @@ __device__ __forceinline__ void store4(void *dst, long idx, const f32x4 &a) {
 // r_seg = sum_i (phi(q_i) a_i) e_i over the segment (token p of the segment
 // weighs gamma^p with a decay), so no separate pass re-reads q and dO.
 // ---------------------------------------------------------------------------
-// Tile type of v and dO: with bf16-pair sweeps they stay bf16 tiles (the
-// values are bf16 exactly), and their fragments meet pairs in two-MFMA
-// products; otherwise the input type.
-template <typename TI>
-using bwd_tv = typename std::conditional<std::is_same<TI, bf16p>::value, __bf16, TI>::type;
+// Tile types.  Input type TI, except with bf16-pair sweeps (TI = bf16p):
+//   bwd_tv  v and dO: bf16 tiles (their values are bf16 exactly), whose
+//           fragments meet pairs in two-MFMA products;
+//   bwd_ts  element of a plane, for strides: bf16;
+//   bwd_pt  the other tiles: two bf16 planes, the remainder plane PL elements
+//           after the value plane (NPL planes in all).
+template <typename TI> constexpr bool bwd_pair() { return std::is_same<TI, bf16p>::value; }
+template <typename TI> using bwd_tv = typename std::conditional<bwd_pair<TI>(), __bf16, TI>::type;
+template <typename TI> using bwd_ts = typename std::conditional<bwd_pair<TI>(), __bf16, TI>::type;
+template <typename TI, int PL> using bwd_pt = typename std::conditional<bwd_pair<TI>(), bf16pl<PL>, TI>::type;
+template <typename TI> constexpr int bwd_npl() { return bwd_pair<TI>() ? 2 : 1; }
 
 template <int DK, int DV, typename TI, bool DEC = false> struct DqSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
-    static constexpr int LK = BwdLd<TI, DK>::TR;   // phi(K): transpose reads
-    static constexpr int LQ = BwdLd<TI, DK>::ROW;  // phi(Q): row reads
+    using TS = bwd_ts<TI>;
+    static constexpr int NPL = bwd_npl<TI>();
+    static constexpr int LK = BwdLd<TS, DK>::TR;   // phi(K): transpose reads
+    static constexpr int LQ = BwdLd<TS, DK>::ROW;  // phi(Q): row reads
     using TV = bwd_tv<TI>;
     static constexpr int LV = BwdLd<TV, DV>::TR;   // V: transpose reads (state), row reads (M)
     static constexpr int LG = BwdLd<TV, DV>::ROW;  // dO: row reads
-    static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[i][j]
-    static constexpr bool LO = sizeof(TI) == 2;     // M kept as value + remainder
-    alignas(16) TI k[CM * LK];
-    alignas(16) TI q[CM * LQ];
+    static constexpr int LM = BwdLd<TS, CM>::ROW;  // M[i][j]
+    static constexpr bool LO = std::is_same<TI, __bf16>::value;  // M kept as value + remainder
+    alignas(16) bwd_pt<TI, CM * LK> k[NPL * CM * LK];
+    alignas(16) bwd_pt<TI, CM * LQ> q[NPL * CM * LQ];
     alignas(16) TV v[CM * LV];
     alignas(16) TV g[CM * LG];
-    alignas(16) TI mh[CM * LM];
-    alignas(16) TI ml[LO ? CM * LM : 4];
+    alignas(16) bwd_pt<TI, CM * LM> mh[NPL * CM * LM];
+    alignas(16) bwd_pt<TI, CM * LM> ml[LO ? CM * LM : 4];
     alignas(16) float red[kBwdWaves][CM][2];  // per-wave partial phi(q).X and phi(q).z
     // decay weights gamma^(i - j) of query i and token j <= i, as value + remainder
     alignas(16) TI dh[DEC ? CM * LM : 8];
@@ -317,7 +327,7 @@ la_bwd_dq_kernel(const BwdParams p) {
     // remainder, so that X = S g and z meet at fp32-level accuracy in
     // X - z (phi(q) . X) / den, whose two terms cancel exactly for a single
     // token (non-causal) and to O(gamma) of their size for a fast decay.
-    constexpr bool SLO = (NC || dec) && sizeof(TC) == 2;
+    constexpr bool SLO = (NC || dec) && std::is_same<TC, __bf16>::value;
     Frag<TC> fragS_lo[SLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
@@ -352,11 +362,11 @@ la_bwd_dq_kernel(const BwdParams p) {
     // per-lane bases of the row-wise reads: row pp, column 4g
     const lds_vptr<TV> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
     const lds_vptr<TV> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
-    const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 16 * eb + 4 * g);
-    const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
-    const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
-    const lds_vptr<TC> dhb = lds_v(sm.dh + (dec ? pp * SM::LM + 4 * g : 0));
-    const lds_vptr<TC> dlb = lds_v(sm.dl + (dec && SM::LO ? pp * SM::LM + 4 * g : 0));
+    const auto qb = lds_v(sm.q + pp * SM::LQ + 16 * eb + 4 * g);
+    const auto mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
+    const auto mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
+    const auto dhb = lds_v(sm.dh + (dec ? pp * SM::LM + 4 * g : 0));
+    const auto dlb = lds_v(sm.dl + (dec && SM::LO ? pp * SM::LM + 4 * g : 0));
 
     for (int ch = 0; ch < nch; ++ch) {
         const int r0 = row_begin + ch * C;
@@ -619,23 +629,25 @@ la_bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 template <int DK, int DV, typename TI> struct DkvSmem {
     static constexpr int CM = bwd_cmax<TI, DK, DV>();
-    static constexpr int LQ = BwdLd<TI, DK>::TR;   // phi(Q): transpose reads (dk, state), row reads (A)
-    static constexpr int LK = BwdLd<TI, DK>::ROW;  // phi(K): row reads
+    using TS = bwd_ts<TI>;
+    static constexpr int NPL = bwd_npl<TI>();
+    static constexpr int LQ = BwdLd<TS, DK>::TR;   // phi(Q): transpose reads (dk, state), row reads (A)
+    static constexpr int LK = BwdLd<TS, DK>::ROW;  // phi(K): row reads
     using TV = bwd_tv<TI>;
     static constexpr int LV = BwdLd<TV, DV>::ROW;  // V: row reads
     static constexpr int LG = BwdLd<TV, DV>::TR;   // dO: transpose reads (dv, state), row reads (M)
-    static constexpr int LR = BwdLd<TI, DV>::TR;   // R[e][c']: transpose reads
-    static constexpr int LM = BwdLd<TI, CM>::ROW;  // M[j][i], A[j][i]
+    static constexpr int LR = BwdLd<TS, DV>::TR;   // R[e][c']: transpose reads
+    static constexpr int LM = BwdLd<TS, CM>::ROW;  // M[j][i], A[j][i]
     static constexpr int RROWS = DK < 32 ? 32 : DK;
-    static constexpr bool LO = sizeof(TI) == 2;
-    alignas(16) TI q[CM * LQ];
-    alignas(16) TI k[CM * LK];
+    static constexpr bool LO = std::is_same<TI, __bf16>::value;
+    alignas(16) bwd_pt<TI, CM * LQ> q[NPL * CM * LQ];
+    alignas(16) bwd_pt<TI, CM * LK> k[NPL * CM * LK];
     alignas(16) TV v[CM * LV];
     alignas(16) TV g[CM * LG];
-    alignas(16) TI R[RROWS * LR];  // copy of the suffix state R[e][c'] for the dv product
-    alignas(16) TI mh[CM * LM];
-    alignas(16) TI ml[LO ? CM * LM : 4];
-    alignas(16) TI at[CM * LM];
+    alignas(16) bwd_pt<TI, RROWS * LR> R[NPL * RROWS * LR];  // copy of the suffix state R[e][c'] for the dv product
+    alignas(16) bwd_pt<TI, CM * LM> mh[NPL * CM * LM];
+    alignas(16) bwd_pt<TI, CM * LM> ml[LO ? CM * LM : 4];
+    alignas(16) bwd_pt<TI, CM * LM> at[NPL * CM * LM];
     alignas(16) float e[CM];  // e = eps * den
     alignas(16) float a[CM];  // a = 1 / den
 };
@@ -699,7 +711,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     // Non-causal, or decayed, with bf16 operands: R also as its rounding
     // remainder, so that R v_j and r meet at fp32-level accuracy (they cancel
     // for a single token, and to O(gamma) of their size for a fast decay).
-    constexpr bool RLO = (NC || dec) && sizeof(TC) == 2;
+    constexpr bool RLO = (NC || dec) && std::is_same<TC, __bf16>::value;
     Frag<TC> fragR_lo[RLO ? NSV : 1];
     auto refresh = [&]() {
 #pragma unroll
@@ -737,13 +749,13 @@ la_bwd_dkdv_kernel(const BwdParams p) {
     }
 
     // per-lane bases of the row-wise reads: row pp, column 4g
-    const lds_vptr<TC> qb = lds_v(sm.q + pp * SM::LQ + 4 * g);
-    const lds_vptr<TC> kb = lds_v(sm.k + pp * SM::LK + 4 * g);
+    const auto qb = lds_v(sm.q + pp * SM::LQ + 4 * g);
+    const auto kb = lds_v(sm.k + pp * SM::LK + 4 * g);
     const lds_vptr<TV> vb = lds_v(sm.v + pp * SM::LV + 4 * g);
     const lds_vptr<TV> gb = lds_v(sm.g + pp * SM::LG + 4 * g);
-    const lds_vptr<TC> mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
-    const lds_vptr<TC> mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
-    const lds_vptr<TC> atb = lds_v(sm.at + pp * SM::LM + 4 * g);
+    const auto mhb = lds_v(sm.mh + pp * SM::LM + 4 * g);
+    const auto mlb = lds_v(sm.ml + (SM::LO ? pp * SM::LM + 4 * g : 0));
+    const auto atb = lds_v(sm.at + pp * SM::LM + 4 * g);
 
     for (int ch = nch - 1; ch >= 0; --ch) {
         const int r0 = row_begin + ch * C;

@@ -114,28 +114,24 @@ __device__ __forceinline__ f32x4 mma(const Frag<float> &a, const Frag<float> &b,
     return c;
 }
 
-// fp32 data as bf16 pairs.  In LDS an element is one 32-bit word: the bf16
-// rounding of the value in the low half and the bf16 rounding of what that
-// leaves out in the high half, about 16 significant bits together (global
-// buffers of this type hold plain fp32).  A product of two such operands is
+// fp32 values as bf16 pairs: a bf16 value and the bf16 rounding of what it
+// leaves out, about 16 significant bits together.  In LDS a pair tile is two
+// bf16 planes of one layout (bf16pl<PL>: the remainder plane PL elements after
+// the value plane), read with the bf16 loaders.  A product of two pairs is
 // hi*hi + hi*lo + lo*hi + lo*lo on the bf16 matrix cores, each product of
 // halves exact in fp32.  lo*lo lies below the pair's own rounding, but without
 // it the product of two pair values is no longer exact, and terms that must
 // cancel (X and z (phi(q) . X) / den of a lone token) miss each other by a
 // part in 2^18.  Four bf16 MFMAs against eight fp32 MFMAs of twice the time
 // each; operands keep about 16 bits instead of 24.
-struct bf16p {
-    uint32_t w;
+struct bf16p {};
+template <int PL> struct bf16pl {
+    __bf16 x;
 };
 
-__device__ __forceinline__ uint32_t bf16p_pack(float x) {
-    const __bf16 h = static_cast<__bf16>(x);
-    const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l)) << 16);
-}
-__device__ __forceinline__ float bf16p_value(uint32_t w) {
-    return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+__device__ __forceinline__ float bf16p_value(float x) {
+    const float h = round_bf16(x);
+    return h + round_bf16(x - h);
 }
 
 template <> struct Frag<bf16p> {
@@ -169,26 +165,11 @@ __device__ __forceinline__ f32x4 mma(const Frag<__bf16> &a, const Frag<bf16p> &b
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.hi, c, 0, 0, 0);
 }
 
-// Eight pair words (slots 0..7) to a fragment: the value halves of two words
-// side by side form one bf16 pair of the hi vector, the remainder halves one
-// of the lo vector (v_perm byte selects).
-__device__ __forceinline__ void bf16p_frag(Frag<bf16p> &f, const uint32_t (&w)[8]) {
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    u32x4v h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x05040100u);
-        l[i] = __builtin_amdgcn_perm(w[2 * i + 1], w[2 * i], 0x07060302u);
-    }
-    f.hi = __builtin_bit_cast(bf16x8, h);
-    f.lo = __builtin_bit_cast(bf16x8, l);
-}
-
 // Round a value to what the operand type can hold (identity for fp32).
 template <typename TC> __device__ __forceinline__ float to_operand(float x);
 template <> __device__ __forceinline__ float to_operand<__bf16>(float x) { return round_bf16(x); }
 template <> __device__ __forceinline__ float to_operand<float>(float x) { return x; }
-template <> __device__ __forceinline__ float to_operand<bf16p>(float x) { return bf16p_value(bf16p_pack(x)); }
+template <> __device__ __forceinline__ float to_operand<bf16p>(float x) { return bf16p_value(x); }
 
 // ---------------------------------------------------------------------------
 // LDS fragment reads.  `row` points at the first element of the operand row
@@ -198,12 +179,6 @@ template <> __device__ __forceinline__ float to_operand<bf16p>(float x) { return
 // Straight assignment: eight consecutive elements starting at row[8g].
 __device__ __forceinline__ void lds_frag_straight(Frag<__bf16> &f, const __bf16 *row, int g) {
     f.v = *reinterpret_cast<const bf16x8 *>(row + 8 * g);
-}
-__device__ __forceinline__ void lds_frag_straight(Frag<bf16p> &f, const bf16p *row, int g) {
-    uint32_t w[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = row[8 * g + t].w;
-    bf16p_frag(f, w);
 }
 __device__ __forceinline__ void lds_frag_straight(Frag<float> &f, const float *row, int g) {
     const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 8 * g);
@@ -294,10 +269,9 @@ __device__ __forceinline__ f32x4 lds_get4(lds_vptr<__bf16> base, int off) {
 __device__ __forceinline__ f32x4 lds_get4(lds_vptr<float> base, int off) {
     return *reinterpret_cast<lds_vptr<f32x4>>(base + off);
 }
-__device__ __forceinline__ f32x4 lds_get4(lds_vptr<bf16p> base, int off) {
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v w = *reinterpret_cast<lds_vptr<u32x4v>>(base + off);
-    return f32x4{bf16p_value(w[0]), bf16p_value(w[1]), bf16p_value(w[2]), bf16p_value(w[3])};
+template <int PL> __device__ __forceinline__ f32x4 lds_get4(lds_vptr<bf16pl<PL>> base, int off) {
+    const lds_vptr<__bf16> b = reinterpret_cast<lds_vptr<__bf16>>(base);
+    return lds_get4(b, off) + lds_get4(b, off + PL);
 }
 
 // Split-assignment fragment: slots 0..3 from base[off..], slots 4..7 from
@@ -311,12 +285,13 @@ __device__ __forceinline__ void lds_frag_split_v(Frag<__bf16> &f, lds_vptr<__bf1
         f.v[t + 4] = b[t];
     }
 }
-__device__ __forceinline__ void lds_frag_split_v(Frag<bf16p> &f, lds_vptr<bf16p> base, int off) {
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v a = *reinterpret_cast<lds_vptr<u32x4v>>(base + off);
-    const u32x4v b = *reinterpret_cast<lds_vptr<u32x4v>>(base + off + 16);
-    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    bf16p_frag(f, w);
+template <int PL> __device__ __forceinline__ void lds_frag_split_v(Frag<bf16p> &f, lds_vptr<bf16pl<PL>> base, int off) {
+    const lds_vptr<__bf16> b = reinterpret_cast<lds_vptr<__bf16>>(base);
+    Frag<__bf16> h, l;
+    lds_frag_split_v(h, b, off);
+    lds_frag_split_v(l, b, off + PL);
+    f.hi = h.v;
+    f.lo = l.v;
 }
 __device__ __forceinline__ void lds_frag_split_v(Frag<float> &f, lds_vptr<float> base, int off) {
     const f32x4 a = *reinterpret_cast<lds_vptr<f32x4>>(base + off);
@@ -335,11 +310,6 @@ __device__ __forceinline__ void lds_put4(__bf16 *p, const f32x4 &x) {
 __device__ __forceinline__ void lds_put4(float *p, const f32x4 &x) {
     *reinterpret_cast<lds_wptr<f32x4>>(lds_w(p)) = x;
 }
-__device__ __forceinline__ void lds_put4(bf16p *p, const f32x4 &x) {
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v w = {bf16p_pack(x[0]), bf16p_pack(x[1]), bf16p_pack(x[2]), bf16p_pack(x[3])};
-    *reinterpret_cast<lds_wptr<u32x4v>>(lds_w(p)) = w;
-}
 
 // Four floats as an operand value (hi) and, for bf16, the bf16 rounding of
 // what that value leaves out (lo): hi + lo carries about 16 significant bits.
@@ -350,7 +320,13 @@ __device__ __forceinline__ void lds_put4_pair(__bf16 *hi, __bf16 *lo, const f32x
     *reinterpret_cast<lds_wptr<bf16x4>>(lds_w(lo)) = __builtin_convertvector(r, bf16x4);
 }
 __device__ __forceinline__ void lds_put4_pair(float *hi, float *, const f32x4 &x) { lds_put4(hi, x); }
-__device__ __forceinline__ void lds_put4_pair(bf16p *hi, bf16p *, const f32x4 &x) { lds_put4(hi, x); }
+template <int PL> __device__ __forceinline__ void lds_put4(bf16pl<PL> *p, const f32x4 &x) {
+    __bf16 *b = reinterpret_cast<__bf16 *>(p);
+    lds_put4_pair(b, b + PL, x);
+}
+template <int PL> __device__ __forceinline__ void lds_put4_pair(bf16pl<PL> *hi, bf16pl<PL> *, const f32x4 &x) {
+    lds_put4(hi, x);
+}
 
 // Transposed reads of a row-major tile (LDS), for operands whose K index is
 // the tile's row index.  The result slots t = 0..3 of the lane at position p
@@ -391,15 +367,15 @@ __device__ __forceinline__ void lds_frag_tr(Frag<float> &f, const float *tile, i
     }
 }
 
-__device__ __forceinline__ void lds_frag_tr(Frag<bf16p> &f, const bf16p *tile, int ld, int row0, int row1,
+template <int PL>
+__device__ __forceinline__ void lds_frag_tr(Frag<bf16p> &f, const bf16pl<PL> *tile, int ld, int row0, int row1,
                                             int col0, int p) {
-    uint32_t w[8];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        w[t] = tile[(row0 + t) * ld + col0 + p].w;
-        w[t + 4] = tile[(row1 + t) * ld + col0 + p].w;
-    }
-    bf16p_frag(f, w);
+    const __bf16 *b = reinterpret_cast<const __bf16 *>(tile);
+    Frag<__bf16> h, l;
+    lds_frag_tr(h, b, ld, row0, row1, col0, p);
+    lds_frag_tr(l, b + PL, ld, row0, row1, col0, p);
+    f.hi = h.v;
+    f.lo = l.v;
 }
 
 template <typename TC> __device__ __forceinline__ void frag_ones(Frag<TC> &f) {
@@ -442,15 +418,8 @@ template <> struct Store<float> {
     }
 };
 
-template <> struct Store<bf16p> {  // global buffers of bf16-pair operands hold fp32
-    static constexpr int VEC = 4;
-    __device__ __forceinline__ static float load(const void *p, long i) {
-        return static_cast<const float *>(p)[i];
-    }
-};
-
-// fp32 values held as two bf16 planes (value, remainder) of the same layout;
-// staged into bf16-pair tiles.
+// fp32 values held in global memory as two bf16 planes (value, remainder) of
+// one layout; staged into bf16-pair tiles.
 struct bf16h {};
 template <> struct Store<bf16h> {
     static constexpr int VEC = 8;  // elements per 16-byte vector of one plane
@@ -470,7 +439,6 @@ __device__ __forceinline__ void unpack16(const uint4 &u, float *out, float) {
     out[2] = __uint_as_float(u.z);
     out[3] = __uint_as_float(u.w);
 }
-__device__ __forceinline__ void unpack16(const uint4 &u, float *out, bf16p) { unpack16(u, out, 0.0f); }
 __device__ __forceinline__ void unpack16(const uint4 &u, float *out, __bf16) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -478,12 +446,6 @@ __device__ __forceinline__ void unpack16(const uint4 &u, float *out, __bf16) {
         out[2 * i] = __uint_as_float(w[i] << 16);
         out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
-}
-
-// A 16-byte vector of fp32 (global layout) as four bf16-pair words.
-__device__ __forceinline__ uint4 bf16p_pack4(const uint4 &u) {
-    return make_uint4(bf16p_pack(__uint_as_float(u.x)), bf16p_pack(__uint_as_float(u.y)),
-                      bf16p_pack(__uint_as_float(u.z)), bf16p_pack(__uint_as_float(u.w)));
 }
 
 // Sum over the four lane groups (lanes p, p+16, p+32, p+48).
