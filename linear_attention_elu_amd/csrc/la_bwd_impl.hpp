@@ -523,6 +523,9 @@ la_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         out[r] = (X[I][r] - Z[I][r] * coef) * inv * (ident ? 1.0f : fminf(fq[r], 1.0f));
+                    // pair sweeps (random features): u = dphi(q) * phi(q), what the
+                    // chain rule through the map takes
+                    if constexpr (bwd_pair<TI>()) out = out * fq;
                     if (valid) store4<TI>(p.dq, orow * DK + 16 * eb + 4 * g, out);
                 }
             }
@@ -892,6 +895,7 @@ la_bwd_dkdv_kernel(const BwdParams p) {
                     f32x4 out;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) out[r] = acc[r] * (ident ? 1.0f : fminf(kd[r], 1.0f));
+                    if constexpr (bwd_pair<TI>()) out = out * kd;  // u = dphi(k) * phi(k)
                     if (valid) store4<TI>(p.dk, orow * DK + 16 * eb + 4 * g, out);
                 }
                 if (has_c) {

@@ -127,8 +127,8 @@ constexpr int kNonCausalChunk = 64;
 //                halves, bf16 [2][BH][N][M] (out unused);
 //   PRF_VJP      out = dx [BH][N][DK] (input type) from x, f = phi(x) and
 //                df = dphi, both fp32;
-//   PRF_VJP_PLANES  the same with f = phi(x) as the two bf16 planes.
-enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2, PRF_VJP_PLANES = 3 };
+//   PRF_VJP_U    the same from x and df = u = dphi * phi (fp32; f unused).
+enum { PRF_PHI = 0, PRF_PHI_F32 = 1, PRF_VJP = 2, PRF_VJP_U = 3 };
 hipError_t launch_prf(bool bf16, int what, const void *x, const void *W, const void *f, const void *df, void *out,
                       long BH, int N, int H, int DK, int M, hipStream_t stream, void *halves = nullptr);
 

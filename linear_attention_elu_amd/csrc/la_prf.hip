@@ -184,15 +184,16 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_kernel(const TC *__restric
 }
 
 // dx^T tiles: acc = W^T[16E.., :] u^T over the m features (u = dphi * phi,
-// both fp32), lane (g, p) ending with elements 16E + 4g + r of token p; then
+// both fp32, or u as given: UG), lane (g, p) ending with elements 16E + 4g + r of token p; then
 // dx = acc - x * sum_r u_r.  With bf16 operands u enters the matrix cores as
 // a bf16 value plus its bf16 remainder, so the product keeps about 16
 // significant bits (W is exact in its storage type).  That precision is
 // needed: phi(x) spans many orders of magnitude across features, so an error
 // of dphi that is small against its row but large against a small entry is
 // multiplied by a large phi_r(x).  The token blocks are pipelined as in
-// la_prf_kernel (phi, dphi and the x elements of the epilogue in flight).
-template <typename TC, int DK, int M, bool PH = false>  // PH: phi_x as two bf16 planes (value, remainder)
+// la_prf_kernel (phi and dphi, or u, and the x elements of the epilogue in
+// flight).
+template <typename TC, int DK, int M, bool UG = false>  // UG: dphi_x holds u = dphi * phi (phi_x unused)
 __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__restrict__ x, const TC *__restrict__ W,
                                                                  const void *__restrict__ phi_x,
                                                                  const float *__restrict__ dphi_x,
@@ -205,23 +206,14 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
     const long bh = blockIdx.x;
     const int first = blockIdx.y * (kPrfSteps * kPrfTokensPerBlock) + 16 * wave;
     struct Regs {
-        Frag<float> ff[NS], fd[NS];
+        Frag<float> ff[UG ? 1 : NS], fd[NS];
         f32x4 xv[NE];
     } rg[2];
     auto load = [&](Regs &r, int step) {
         const long row = bh * N + min(first + kPrfTokensPerBlock * step + pp, N - 1);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            if constexpr (PH) {  // phi = value plane + remainder plane (bf16 each)
-                const __bf16 *ph = static_cast<const __bf16 *>(phi_x) + row * M + 32 * s + 8 * g;
-                float hv[8], lv[8];
-                unpack16(*reinterpret_cast<const uint4 *>(ph), hv, __bf16());
-                unpack16(*reinterpret_cast<const uint4 *>(ph + (long)gridDim.x * N * M), lv, __bf16());
-#pragma unroll
-                for (int u = 0; u < 8; ++u) r.ff[s].set(u, hv[u] + lv[u]);
-            } else {
-                frag_global8(r.ff[s], static_cast<const float *>(phi_x) + row * M + 32 * s + 8 * g);
-            }
+            if constexpr (!UG) frag_global8(r.ff[s], static_cast<const float *>(phi_x) + row * M + 32 * s + 8 * g);
             frag_global8(r.fd[s], dphi_x + row * M + 32 * s + 8 * g);
         }
 #pragma unroll
@@ -245,7 +237,9 @@ __global__ void __launch_bounds__(kPrfThreads) la_prf_vjp_kernel(const TC *__res
             Frag<TC> fu, fu_lo;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float val = cr.ff[s].get(u) * cr.fd[s].get(u);
+                float val;
+                if constexpr (UG) val = cr.fd[s].get(u);
+                else val = cr.ff[s].get(u) * cr.fd[s].get(u);
                 su += val;
                 fu.set(u, val);
                 if constexpr (LO) fu_lo.set(u, val - fu.get(u));
@@ -276,7 +270,7 @@ hipError_t launch_prf_t(int what, const void *x, const void *W, const void *f, c
     if (what == PRF_VJP)
         la_prf_vjp_kernel<TC, DK, M><<<grid, kPrfThreads, 0, stream>>>(xc, wc, f, static_cast<const float *>(df),
                                                                         static_cast<TC *>(out), N, H);
-    else if (what == PRF_VJP_PLANES)
+    else if (what == PRF_VJP_U)
         la_prf_vjp_kernel<TC, DK, M, true><<<grid, kPrfThreads, 0, stream>>>(xc, wc, f, static_cast<const float *>(df),
                                                                               static_cast<TC *>(out), N, H);
     else if (what == PRF_PHI_F32 && halves)
@@ -544,7 +538,7 @@ la_status la_bwd_causal_fm(const void *q, const void *k, const void *v, const vo
     }
     d.ws = reinterpret_cast<float *>(at(ws, l.inner));
     if ((e = la::run_bwd(d)) != hipSuccess) return la::from_hip(e);
-    const int vjp = bf ? la::PRF_VJP_PLANES : la::PRF_VJP;
+    const int vjp = bf ? la::PRF_VJP_U : la::PRF_VJP;  // the pair sweeps write u = dphi * phi
     e = la::launch_prf(bf, vjp, q, W, at(ws, l.fq), at(ws, l.dfq), dq, BH, N, H, d_k, m, stream);
     if (e == hipSuccess) e = la::launch_prf(bf, vjp, k, W, at(ws, l.fk), at(ws, l.dfk), dk, BH, N, H, d_k, m, stream);
     return la::from_hip(e);
