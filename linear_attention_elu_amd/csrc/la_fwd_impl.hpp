@@ -33,7 +33,8 @@
 // workgroup per CU.  Wider heads in the causal and read-out passes, and fp32,
 // whose compute waves need more registers than two waves per SIMD leave, use
 // four waves that do both jobs in turn (stage chunk c + 1, compute chunk c)
-// with one register set.  Chunks
+// with one register set, or two (loads two chunks ahead) in the bf16 causal
+// loop without decay.  Chunks
 // whose rows are all valid run an unrolled loop (buffer and register-set
 // indices are constants) with fixed per-lane offsets from a uniform base and
 // no row masks; the last chunks run a general loop with clamped loads.
@@ -179,6 +180,9 @@ la_chunk_kernel(const FwdParams p) {
     // keep two.  A power of two, and even where NBUF = 2.
     constexpr int NSET = (SPLIT && MODE == MODE_CAUSAL) ? 4 : 2;
     static_assert(NSET == 2 || NSET == 4 || NSET == 8, "register sets: 2, 4 or 8");
+    // Four-wave causal loop on bf16 with two buffers: loads two chunks ahead
+    // (both register sets) instead of one; decayed kernels would spill.
+    constexpr bool PF2 = !SPLIT && MODE == MODE_CAUSAL && !DECAY && sizeof(TI) == 2 && T::NBUF == 2;
     constexpr int VEC = Store<TI>::VEC;
     constexpr int NE = DK / 16;            // feature tiles
     constexpr int NSE = (DK + 31) / 32;    // feature K steps
@@ -955,6 +959,44 @@ la_chunk_kernel(const FwdParams p) {
             if (j < nfull) compute(b, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, j, CT, part, o, d); });
             else compute(b, rows_of(j), [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, j, rows_of(j), part, o, d); });
             if (NBUF == 1 && j + 1 < nch) __syncthreads();  // the staging waves refill the single buffer
+        }
+    } else if constexpr (PF2) {
+        // ---- four waves in both roles, loads two chunks ahead: chunk j is
+        // loaded into register set j & 1; step ch stages chunk ch + 1 into
+        // buffer (ch + 1) & 1, refills its set with chunk ch + 3 and computes
+        // chunk ch.  Absent chunks load clamped rows and are never staged. ----
+        load_any(S0t{}, 0);
+        load_any(S1t{}, 1);
+        __syncthreads();  // the zero fill is complete before any tile write
+        stage(S0t{}, Part{}, 0, rows_of(0));
+        load_any(S0t{}, 2);
+        __syncthreads();
+        int ch = 0;
+        // Pairs of full steps: chunks ch .. ch + 4 are full.
+        for (; ch + 4 < nfull; ch += 2) {
+            stage(S1t{}, Full{}, 1, CT);
+            load(S1t{}, Full{}, ch + 3);
+            compute(0, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+            __syncthreads();
+            stage(S0t{}, Full{}, 0, CT);
+            load(S0t{}, Full{}, ch + 4);
+            compute(1, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch + 1, CT, part, o, d); });
+            __syncthreads();
+        }
+        for (; ch < nch; ++ch) {
+            const int b = ch & 1;
+            if (ch + 1 < nch) {
+                static_for<2>([&](auto u) LA_INLINE {
+                    if (((ch + 1) & 1) == decltype(u)::value) {
+                        if (ch + 1 < nfull) stage(u, Full{}, b ^ 1, CT);
+                        else stage(u, Part{}, b ^ 1, rows_of(ch + 1));
+                        if (ch + 3 < nch) load_any(u, ch + 3);
+                    }
+                });
+            }
+            if (ch < nfull) compute(b, CT, [&](int part, auto &o, auto &d) LA_INLINE { store_out(Full{}, ch, CT, part, o, d); });
+            else compute(b, rows_of(ch), [&](int part, auto &o, auto &d) LA_INLINE { store_out(Part{}, ch, rows_of(ch), part, o, d); });
+            __syncthreads();
         }
     } else {
         // ---- four waves in both roles: stage chunk c + 1, compute chunk c ----
