@@ -40,6 +40,10 @@ inline long fine_target(long BH, long want, long resident) {
 // apiece), against 26.9 us with a separate total pass.
 constexpr int kNonCausalAggSegments = 4;
 
+// Causal chunks per (b, h) up to which the split-layout forward runs one
+// segment per (b, h) (no aggregate pass and no scan).
+constexpr long kOneSegmentChunks = 16;
+
 // DECAY: the causal form with a per-head decay (d.gamma non-null).  PRF: the
 // random-feature map in the staging waves (d.phi_id 2, d.W).  CT: the chunk
 // of the causal and read-out kernels; CTA: that of the aggregate pass.
@@ -53,7 +57,13 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     // pass uses fine segments; a causal segment is a run of `mult` of them.
     const long target_main = causal ? chunk_resident<DK, DV, TI, MODE_CAUSAL, CT, OBF, DECAY, PRF>()
                                     : chunk_resident<DK, DV, TI, MODE_APPLY, CT, OBF, false, PRF>();
-    const long want_main = (target_main + BH - 1) / BH;
+    long want_main = (target_main + BH - 1) / BH;
+    // A short sequence runs as one segment per (b, h) in the split layout:
+    // at B=8, H=8, d=64, C=64 the three launches of a four-way split took
+    // 20.3 us at N=512 and 26.5 at N=1024, one segment 13.8 and 23.8; from
+    // N=2048 (32 chunks) on the split is faster (35.4 against 42.7 us).
+    if (causal && fwd_split<DK, DV, TI, MODE_CAUSAL, DECAY>() && (d.N + CT - 1) / CT <= kOneSegmentChunks)
+        want_main = 1;
     long target_agg = chunk_resident<DK, DV, TI, MODE_AGG, CTA, false, DECAY, PRF>();
     if (causal) target_agg = fine_target(BH, want_main, target_agg);
     // A workspace holding at most d.ws_states segment states (a fixed scratch):

@@ -24,6 +24,11 @@ CAUSAL_CASES = [
     (1, 1, 1000, 128, 128, 64),
     (1, 2, 777, 32, 64, 64),
     (3, 1, 96, 16, 16, 32),
+    # bf16 at d <= 64 runs up to 16 chunks per (batch, head) as one segment:
+    # both sides of that bound, and a split of several segments at small width
+    (1, 2, 1024, 64, 64, 64),
+    (1, 2, 1025, 64, 64, 64),
+    (2, 1, 2100, 32, 16, 64),
 ]
 
 
