@@ -58,8 +58,8 @@ hipError_t run_bwd_nc_ct(const BwdDesc &d) {
     const long target_kv = resident_workgroups(reinterpret_cast<const void *>(dkdv_kernel), occ_kv, kBwdThreads);
     // a few aggregate segments per (b, h), as in the non-causal forward (a
     // target within kMaxTargetWg keeps Pf within the workspace the query sized)
-    const long target_agg = BH * (long)kNonCausalAggSegments < kMaxTargetWg ? BH * (long)kNonCausalAggSegments
-                                                                             : kMaxTargetWg;
+    const long target_agg = BH * (long)nc_agg_segments<DK, DV>() < kMaxTargetWg ? BH * (long)nc_agg_segments<DK, DV>()
+                                                                                 : kMaxTargetWg;
     int Lf = 0;
     const int Pf = plan_segments(BH, d.N, d.C, target_agg, &Lf);
 

@@ -35,10 +35,12 @@ inline long fine_target(long BH, long want, long resident) {
 }
 
 // Aggregate segments per (b, h) of the non-causal form (at most).  At B=4,
-// H=8, N=4096, d=64 the forward took 29.1 us with 2, 23.2 with 4, 22.8 with 8
-// and 29.2 with 16 (each read-out workgroup sums them: d_k (d_v + 1) floats
-// apiece), against 26.9 us with a separate total pass.
-constexpr int kNonCausalAggSegments = 4;
+// H=8, N=4096, d=64 the forward took 29.1 us with 2, 24.6 with 4, 23.6 with
+// 6, 23.8 with 8 and 29.2 with 16 (each read-out workgroup sums them: d_k
+// (d_v + 1) floats apiece), against 26.9 us with a separate total pass; the
+// backward 66.1 us with 4, 65.2 with 6, 66.5 with 8.  A 128-wide state
+// (66 KB) keeps four, so that the read-out prologues stay short.
+template <int DK, int DV> constexpr int nc_agg_segments() { return (DK <= 64 && DV <= 64) ? 6 : 4; }
 
 // Causal chunks per (b, h) up to which the split-layout forward runs one
 // segment per (b, h) (no aggregate pass and no scan).
@@ -125,8 +127,8 @@ hipError_t run_fwd_ct(const FwdDesc &d, bool causal) {
     // read-out workgroup in its prologue (no total pass, no extra launch).
     int Ln = 0;
     // (a target within kMaxTargetWg keeps Pn within the workspace the query sized)
-    const long target_nc = BH * (long)kNonCausalAggSegments < kMaxTargetWg ? BH * (long)kNonCausalAggSegments
-                                                                            : kMaxTargetWg;
+    const long target_nc = BH * (long)nc_agg_segments<DK, DV>() < kMaxTargetWg ? BH * (long)nc_agg_segments<DK, DV>()
+                                                                                : kMaxTargetWg;
     const int Pn = plan_segments(BH, d.N, d.C, target_nc, &Ln);
     p.seg_out = d.ws;
     p.L = Ln;
