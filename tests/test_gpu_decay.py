@@ -20,6 +20,8 @@ DECAY_CASES = [
     (1, 2, 700, 128, 128, 64),
     (2, 2, 5000, 64, 64, 64),   # several segments per (batch, head): the scan decays too
     (1, 3, 3001, 64, 32, 32),
+    (1, 2, 1024, 64, 64, 64),   # bf16 at d <= 64: 16 chunks run as one segment,
+    (1, 2, 1025, 64, 64, 64),   # 17 as several
 ]
 
 

@@ -60,6 +60,8 @@ PRF_CASES = [  # (B, H, N, d_k, d_v, m, C)
     (1, 1, 130, 64, 16, 64, 64),
     (1, 2, 300, 32, 32, 32, 64),    # m = d_k = 32 in the chunk kernels
     (2, 1, 77, 32, 64, 32, 64),
+    (1, 2, 1024, 64, 64, 64, 64),   # bf16 at d <= 64: 16 chunks run as one segment,
+    (1, 2, 1025, 64, 64, 64, 64),   # 17 as several
 ]
 
 
